@@ -1,0 +1,8 @@
+"""CPU oracle (test infrastructure): fp64 attention forward.
+
+Only the tests, the package smoke check and the bench's CPU-baseline leg
+may import this package.  The product path never does.
+"""
+from .attention_fp64 import attention_ref, default_workers, algorithmic_flops
+
+__all__ = ["attention_ref", "default_workers", "algorithmic_flops"]

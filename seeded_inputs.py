@@ -1,0 +1,117 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is the only code that both the CPU oracle side (tests, the
+bench's CPU baseline) and the HIP side (tests, bench, smoke) use.  It draws
+i.i.d. Gaussian Q, K, V from a numpy ``default_rng(seed)`` and, for the bf16
+workloads, rounds them to bfloat16 with round-to-nearest-even.  It contains
+no attention arithmetic: no products, no softmax, no masking.
+
+The value distributions follow the pages' own test and benchmark inputs
+(standard normal Q, K, V: "第 08 章: Flash Attention——分块注意力",
+chuoer47.github.io, the test and benchmark harness of its listing), with the
+per-workload sigma and sizes listed in ``WORKLOADS``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Lq: int
+    Lk: int
+    d: int
+    dtype: str            # "bf16" or "fp32"
+    modes: tuple          # subset of ("noncausal", "causal")
+    seed: int
+    sigma_qk: float = 1.0
+    sigma_v: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        # 1/sqrt(d), rounded to fp32: the value both sides receive.
+        return float(np.float32(1.0) / np.sqrt(np.float32(self.d)))
+
+
+# The five synthetic workloads (seeds 1..5, drawn in the order Q, K, V).
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 2, 128, 128, 64, "fp32",
+                          ("noncausal", "causal"), 1),
+    "bf16_causal_1k_d64": Workload("bf16_causal_1k_d64", 4, 16, 1024, 1024, 64,
+                                   "bf16", ("causal",), 2),
+    "bf16_4k_d128": Workload("bf16_4k_d128", 2, 32, 4096, 4096, 128, "bf16",
+                             ("noncausal", "causal"), 3),
+    "bf16_causal_16k_d128": Workload("bf16_causal_16k_d128", 1, 16, 16384,
+                                     16384, 128, "bf16", ("causal",), 4),
+    "bf16_peaky_d256_ragged": Workload("bf16_peaky_d256_ragged", 1, 8, 8000,
+                                       8192, 256, "bf16", ("noncausal",), 5,
+                                       sigma_qk=3.0),
+}
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    Inputs are finite Gaussian draws, so NaN handling is not needed; an
+    assertion guards that assumption.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert np.isfinite(x).all()
+    bits = x.view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def draw(seed: int, B: int, H: int, Lq: int, Lk: int, d: int,
+         sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """Draw fp32 Q [B,H,Lq,d], K [B,H,Lk,d], V [B,H,Lk,d] in that order."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, Lq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, Lk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, Lk, d), dtype=np.float32)
+    if sigma_qk != 1.0:
+        q *= np.float32(sigma_qk)
+        k *= np.float32(sigma_qk)
+    if sigma_v != 1.0:
+        v *= np.float32(sigma_v)
+    return q, k, v
+
+
+def make_inputs(seed: int, B: int, H: int, Lq: int, Lk: int, d: int,
+                dtype: str = "bf16", sigma_qk: float = 1.0,
+                sigma_v: float = 1.0):
+    """Return (q, k, v) as the device-side storage arrays.
+
+    dtype "bf16": uint16 arrays holding bfloat16 bits (RNE from the fp32
+    draw).  dtype "fp32": float32 arrays.  The oracle side widens these with
+    ``widen`` so both sides see identical values.
+    """
+    q, k, v = draw(seed, B, H, Lq, Lk, d, sigma_qk, sigma_v)
+    if dtype == "bf16":
+        return round_to_bf16_bits(q), round_to_bf16_bits(k), round_to_bf16_bits(v)
+    if dtype == "fp32":
+        return q, k, v
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def widen(x: np.ndarray) -> np.ndarray:
+    """Storage array (bf16 bits or fp32) -> exact float64 values."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, w.dtype,
+                       w.sigma_qk, w.sigma_v)

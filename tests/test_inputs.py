@@ -1,0 +1,48 @@
+"""The seeded input generator: bf16 rounding and reproducibility."""
+import numpy as np
+import torch
+
+from seeded_inputs import (WORKLOADS, bf16_bits_to_f32, draw, make_inputs,
+                           round_to_bf16_bits, widen)
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * 3,
+        # ties and near-ties: values exactly halfway between bf16 neighbours
+        (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x7FFF).view(np.float32),
+    ])
+    ours = round_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy()
+    np.testing.assert_array_equal(ours.view(np.int16), theirs)
+    # widening is exact
+    back = bf16_bits_to_f32(ours)
+    np.testing.assert_array_equal(
+        back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_draw_is_reproducible_and_ordered():
+    q1, k1, v1 = draw(7, 1, 2, 5, 6, 4)
+    q2, k2, v2 = draw(7, 1, 2, 5, 6, 4)
+    np.testing.assert_array_equal(q1, q2)
+    rng = np.random.default_rng(7)
+    np.testing.assert_array_equal(q1, rng.standard_normal((1, 2, 5, 4), dtype=np.float32))
+    np.testing.assert_array_equal(k1, rng.standard_normal((1, 2, 6, 4), dtype=np.float32))
+    np.testing.assert_array_equal(v1, rng.standard_normal((1, 2, 6, 4), dtype=np.float32))
+
+
+def test_sigma_and_widen():
+    q, k, v = make_inputs(5, 1, 1, 64, 64, 8, "bf16", sigma_qk=3.0)
+    qf, kf, vf = draw(5, 1, 1, 64, 64, 8, sigma_qk=3.0)
+    np.testing.assert_array_equal(widen(q), torch.from_numpy(qf).to(torch.bfloat16).double().numpy())
+    assert widen(v).dtype == np.float64
+    assert abs(np.std(qf) - 3.0) < 0.5 and abs(np.std(vf) - 1.0) < 0.2
+
+
+def test_workload_table():
+    assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5]
+    w = WORKLOADS["bf16_peaky_d256_ragged"]
+    assert (w.Lq, w.Lk, w.d, w.sigma_qk) == (8000, 8192, 256, 3.0)
+    assert np.float32(WORKLOADS["bf16_4k_d128"].scale) == np.float32(1 / np.sqrt(np.float32(128)))

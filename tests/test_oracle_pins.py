@@ -1,0 +1,226 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks the oracle against something the pages or the mathematics
+fix independently of the oracle's own code: a hand-worked example with exact
+rational answers, a brute-force evaluation of the definition, a library
+routine (torch's fp64 scaled-dot-product attention, scipy's logsumexp),
+closed forms, and invariants of softmax.  ``test_oracle_mutants.py`` plants
+plausible mistakes in copies of the oracle and checks these pins catch them.
+"""
+import math
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from oracle import attention_ref
+from tests.oracle_pin_checks import (
+    brute_force, golden_cases, online_blocked, rng_qkv,
+)
+
+GOLDEN = Path(__file__).parent / "golden" / "hand_softmax_weights.txt"
+
+
+# --- hand-worked example -------------------------------------------------
+
+@pytest.mark.parametrize("case", ["noncausal", "causal", "rect_causal"])
+def test_golden_hand_example(case):
+    g = golden_cases(GOLDEN)
+    q, k, v, scale = g["q"], g["k"], g["v"], g["scale"]
+    if case == "rect_causal":
+        q = q[:2]
+    causal = case != "noncausal"
+    O, L = attention_ref(q[None, None], k[None, None], v[None, None],
+                         causal, scale)
+    np.testing.assert_allclose(O[0, 0], g[f"{case} O"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L[0, 0], g[f"{case} LSE"], rtol=0, atol=1e-12)
+
+
+# --- brute force on tiny inputs ------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lk,d", [(1, 1, 1), (3, 5, 2), (5, 3, 4),
+                                     (8, 8, 3), (7, 2, 4), (2, 8, 1)])
+def test_brute_force(causal, Lq, Lk, d):
+    for seed in range(3):
+        q, k, v = rng_qkv(seed, 2, 1, Lq, Lk, d)
+        scale = 0.7
+        O, L = attention_ref(q, k, v, causal, scale)
+        for b in range(2):
+            Ob, Lb = brute_force(q[b, 0], k[b, 0], v[b, 0], causal, scale)
+            np.testing.assert_allclose(O[b, 0], Ob, rtol=0, atol=1e-13)
+            np.testing.assert_allclose(L[b, 0], Lb, rtol=0, atol=1e-13)
+
+
+# --- library routines ----------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Lq,Lk,d", [(2, 3, 37, 37, 16), (1, 2, 64, 100, 8),
+                                         (1, 1, 90, 33, 32)])
+def test_sdpa_library(causal, B, H, Lq, Lk, d):
+    import torch
+    import torch.nn.functional as F
+    q, k, v = rng_qkv(11, B, H, Lq, Lk, d)
+    scale = 1.0 / math.sqrt(d)
+    O, _ = attention_ref(q, k, v, causal, scale)
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=causal, scale=scale).numpy()
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_scipy_logsumexp(causal):
+    from scipy.special import logsumexp
+    q, k, v = rng_qkv(5, 1, 2, 40, 50, 8)
+    scale = 0.35
+    _, L = attention_ref(q, k, v, causal, scale)
+    s = np.einsum("bhid,bhjd->bhij", q, k) * scale
+    if causal:
+        mask = np.arange(50)[None, :] <= np.arange(40)[:, None]
+        s = np.where(mask, s, -np.inf)
+    np.testing.assert_allclose(L, logsumexp(s, axis=-1), rtol=0, atol=1e-12)
+
+
+# --- softmax invariants --------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows(causal):
+    q, k, v = rng_qkv(3, 1, 2, 33, 45, 8, sigma=3.0)
+    scale = 0.5
+    O, L, P = attention_ref(q, k, v, causal, scale, return_p=True)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert (P >= 0).all() and (P <= 1).all()
+    s = np.einsum("bhid,bhjd->bhij", q, k) * scale
+    vis = np.ones_like(s, dtype=bool)
+    if causal:
+        vis = np.broadcast_to(np.arange(45)[None, :] <= np.arange(33)[:, None],
+                              s.shape)
+    # P is recovered from the scores and LSE alone (chuoer47 section 3:
+    # softmax(x_i) = exp(x_i - LSE))
+    rebuilt = np.where(vis, np.exp(s - L[..., None]), 0.0)
+    np.testing.assert_allclose(P, rebuilt, rtol=0, atol=1e-12)
+    m = np.where(vis, s, -np.inf).max(-1)
+    n = vis.sum(-1)
+    assert (L >= m - 1e-12).all() and (L <= m + np.log(n) + 1e-12).all()
+    # O lies in the convex hull of the visible values, per coordinate
+    for b in range(1):
+        for h in range(2):
+            for i in range(33):
+                vv = v[b, h][vis[b, h, i]]
+                assert (O[b, h, i] >= vv.min(0) - 1e-12).all()
+                assert (O[b, h, i] <= vv.max(0) + 1e-12).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(causal):
+    # adding the same vector u to every key shifts row i's scores by
+    # scale*q_i.u: P and O unchanged, LSE shifted by that amount
+    q, k, v = rng_qkv(8, 1, 2, 30, 30, 6)
+    u = np.random.default_rng(1).standard_normal(6)
+    scale = 0.4
+    O1, L1 = attention_ref(q, k, v, causal, scale)
+    O2, L2 = attention_ref(q, k + u, v, causal, scale)
+    np.testing.assert_allclose(O2, O1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L2, L1 + scale * (q @ u), rtol=0, atol=1e-12)
+
+
+def test_permutation_equivariance():
+    q, k, v = rng_qkv(9, 1, 1, 20, 24, 5)
+    O, L = attention_ref(q, k, v, False, 0.6)
+    pk = np.random.default_rng(2).permutation(24)
+    O2, L2 = attention_ref(q, k[:, :, pk], v[:, :, pk], False, 0.6)
+    np.testing.assert_allclose(O2, O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L2, L, rtol=0, atol=1e-12)
+    pq = np.random.default_rng(3).permutation(20)
+    O3, L3 = attention_ref(q[:, :, pq], k, v, False, 0.6)
+    np.testing.assert_allclose(O3, O[:, :, pq], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L3, L[:, :, pq], rtol=0, atol=1e-12)
+
+
+def test_causality():
+    q, k, v = rng_qkv(10, 1, 1, 16, 16, 4)
+    O, L = attention_ref(q, k, v, True, 0.5)
+    for i in [0, 5, 14]:
+        k2, v2 = k.copy(), v.copy()
+        k2[:, :, i + 1:] += 7.0
+        v2[:, :, i + 1:] -= 3.0
+        O2, L2 = attention_ref(q, k2, v2, True, 0.5)
+        np.testing.assert_array_equal(O2[:, :, i], O[:, :, i])
+        np.testing.assert_array_equal(L2[:, :, i], L[:, :, i])
+        assert np.abs(O2[:, :, i + 1:] - O[:, :, i + 1:]).max() > 1e-3
+
+
+# --- closed forms --------------------------------------------------------
+
+def test_scale_zero_means():
+    q, k, v = rng_qkv(12, 1, 2, 9, 13, 3)
+    O, L = attention_ref(q, k, v, False, 0.0)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(2, keepdims=True),
+                                                  O.shape), atol=1e-13)
+    np.testing.assert_allclose(L, math.log(13), atol=1e-13)
+    Oc, Lc = attention_ref(q, k, v, True, 0.0)
+    prefix = np.cumsum(v, axis=2)[:, :, :9] / np.arange(1, 10)[:, None]
+    np.testing.assert_allclose(Oc, prefix, atol=1e-13)
+    np.testing.assert_allclose(Lc, np.broadcast_to(np.log(np.arange(1, 10)),
+                                                   Lc.shape), atol=1e-13)
+
+
+def test_causal_first_row_and_single_key():
+    q, k, v = rng_qkv(13, 2, 2, 11, 11, 7)
+    O, L = attention_ref(q, k, v, True, 0.3)
+    np.testing.assert_array_equal(O[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(L[:, :, 0],
+                               0.3 * (q[:, :, 0] * k[:, :, 0]).sum(-1),
+                               atol=1e-13)
+    O1, L1 = attention_ref(q, k[:, :, :1], v[:, :, :1], False, 0.3)
+    np.testing.assert_array_equal(O1, np.broadcast_to(v[:, :, :1], O1.shape))
+    np.testing.assert_allclose(L1, 0.3 * (q * k[:, :, :1]).sum(-1), atol=1e-13)
+
+
+def test_identical_keys_uniform_and_one_hot():
+    q, k, v = rng_qkv(14, 1, 1, 6, 10, 4)
+    kk = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    O, _ = attention_ref(q, kk, v, False, 0.9)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(2, keepdims=True),
+                                                  O.shape), atol=1e-13)
+    # one key dominates each row by a gap of >100 in score: O = that value
+    kp = np.zeros((1, 1, 10, 4))
+    qp = np.zeros((1, 1, 6, 4))
+    for i in range(6):
+        qp[0, 0, i, i % 4] = 1.0
+    for j in range(4):
+        kp[0, 0, 2 * j + 1, j] = 400.0
+    O, L = attention_ref(qp, kp, v, False, 1.0)
+    for i in range(6):
+        j = 2 * (i % 4) + 1
+        np.testing.assert_allclose(O[0, 0, i], v[0, 0, j], atol=1e-12)
+        np.testing.assert_allclose(L[0, 0, i], 400.0, atol=1e-12)
+
+
+# --- the online recurrence the kernel runs -------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [1, 7, 16, 64, 1000])
+def test_online_recurrence_equals_oracle(causal, block):
+    q, k, v = rng_qkv(15, 1, 2, 70, 90, 8, sigma=2.0)
+    O, L = attention_ref(q, k, v, causal, 0.45)
+    for h in range(2):
+        Ob, Lb = online_blocked(q[0, h], k[0, h], v[0, h], causal, 0.45, block)
+        np.testing.assert_allclose(Ob, O[0, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(Lb, L[0, h], rtol=0, atol=1e-12)
+
+
+# --- evaluation helpers --------------------------------------------------
+
+def test_row_subset_and_workers_agree():
+    q, k, v = rng_qkv(16, 2, 3, 300, 310, 16)
+    O, L = attention_ref(q, k, v, True, 0.25, chunk=64)
+    rows = np.array([0, 1, 63, 64, 299, 150])
+    Os, Ls = attention_ref(q, k, v, True, 0.25, rows=rows, chunk=4)
+    np.testing.assert_allclose(Os, O[:, :, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Ls, L[:, :, rows], rtol=0, atol=1e-13)
+    Ow, Lw = attention_ref(q, k, v, True, 0.25, chunk=64, workers=4)
+    np.testing.assert_array_equal(Ow, O)
+    np.testing.assert_array_equal(Lw, L)
