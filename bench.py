@@ -1,0 +1,226 @@
+"""Benchmark of the MI355X FlashAttention-2 forward (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward pass (one ``fa_fwd`` launch) over the whole workload
+with Q, K, V already resident in HBM.  W untimed steps, then exactly K timed
+steps bracketed by device synchronisation; rank 0 prints one JSON line.
+
+Throughput counts the two matmuls only: 4*B*H*Lq*Lk*d flops, halved for
+causal ("第 08 章: Flash Attention——分块注意力" (chuoer47.github.io), its
+benchmark harness).  The roofline object prices that against MI355X's dense
+bf16 MFMA peak (2.5 PFLOP/s).  The CPU baseline times the fp64 oracle on a
+bounded sample of the same workload (whole heads) on this host's cores; it
+is a reported baseline only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA / fp32
+DEFAULT_WORKLOAD = "bf16_causal_16k_d128"
+KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
+                             "fa_fwd_kernel.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this workload, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"fa_fwd_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def to_device(x: np.ndarray):
+    """Host storage array (bf16 bits as uint16, or fp32) -> GPU tensor."""
+    import torch
+    if x.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16))
+        return t.view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def flops_of(w, causal: bool) -> float:
+    f = 4.0 * w.B * w.H * w.Lq * w.Lk * w.d
+    return f / 2 if causal else f
+
+
+def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None):
+    """Time the oracle on whole (batch, head) slices of the workload, one
+    after another, until ``budget_s`` of host time is spent or all slices
+    are done.  Also reports the GPU result's error on that sample."""
+    from oracle import algorithmic_flops, attention_ref, default_workers
+    from seeded_inputs import widen
+    cores = default_workers()
+    O_gpu, L_gpu = gpu_out
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if max_heads:
+        slices = slices[:max_heads]
+    per_slice = algorithmic_flops(np.arange(w.Lq), w.Lk, w.d, causal)
+    spent, done, eo, el = 0.0, 0, 0.0, 0.0
+    for b, h in slices:
+        qs, ks, vs = (widen(x[b:b + 1, h:h + 1]) for x in (q, k, v))
+        t0 = time.perf_counter()
+        O_ref, L_ref = attention_ref(qs, ks, vs, causal, w.scale,
+                                     workers=cores, chunk=256)
+        spent += time.perf_counter() - t0
+        done += 1
+        eo = max(eo, float(np.abs(widen(O_gpu[b:b + 1, h:h + 1]) - O_ref).max()))
+        el = max(el, float(np.abs(L_gpu[b:b + 1, h:h + 1].astype(np.float64)
+                                  - L_ref).max()))
+        if spent >= budget_s:
+            break
+    fl = done * per_slice
+    return {
+        "value": fl / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done} of {w.B * w.H} (batch, head) slices, all "
+                   f"{w.Lq} query rows each, fp64 numpy oracle, "
+                   f"{spent:.2f} s wall"),
+        "seconds": spent,
+        "sample_flops": fl,
+    }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "slices": done}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mode", choices=["causal", "noncausal"], default=None,
+                    help="default: the workload's first mode")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="host seconds for the CPU-baseline sample")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="cap on (batch, head) slices in the CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not "
+              "supported (the forward shards over batch*head with no "
+              "communication; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_io_aware_08_amd as fa
+    from seeded_inputs import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[a.workload]
+    mode = a.mode or w.modes[0]
+    causal = mode == "causal"
+    log(f"bench: workload {w.name} mode {mode} steps {a.steps} warmup {a.warmup}")
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    od = torch.empty((w.B, w.H, w.Lq, w.d), dtype=tdt, device="cuda")
+    ld = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal),
+            w.scale, stream)
+
+    for _ in range(a.warmup):
+        fn(*args)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        starts[i].record(stream)
+        fn(*args)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
+    ms_kernel = float(np.mean(per))
+    ms_step = wall * 1e3 / a.steps
+    flops = flops_of(w, causal)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    log(f"bench: kernel {ms_kernel:.4f} ms (min {min(per):.4f}, median "
+        f"{float(np.median(per)):.4f}), step {ms_step:.4f} ms, "
+        f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.2f}% of {peak} peak")
+
+    gpu_out = None
+    cpu = None
+    parity = None
+    if not a.no_cpu_baseline:
+        o_np = od.view(torch.int16).cpu().numpy().view(np.uint16) \
+            if w.dtype == "bf16" else od.cpu().numpy()
+        gpu_out = (o_np, ld.cpu().numpy())
+        log("bench: CPU oracle baseline ...")
+        cpu, parity = cpu_baseline(w, causal, q, k, v, gpu_out, a.cpu_budget,
+                                   a.cpu_heads)
+        log(f"bench: oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores "
+            f"-> {cpu['value'] * 1e3:.2f} GFLOP/s; parity on sample {parity}")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_mfma_peak": round(100 * value / peak, 3),
+        "config": {"workload": f"{w.name} ({mode})", "B": w.B, "H": w.H,
+                   "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "causal": causal,
+                   "scale": w.scale, "seed": w.seed,
+                   "sigma_qk": w.sigma_qk, "sigma_v": w.sigma_v},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 5),
+                     "traffic": traffic_from_profiles(w.name),
+                     "kernel_ms": round(ms_kernel, 5),
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None if cpu is None else {
+            k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
+    }
+    if parity is not None:
+        line["parity_on_cpu_sample"] = parity
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

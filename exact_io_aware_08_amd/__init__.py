@@ -1,0 +1,164 @@
+"""MI355X (gfx950) FlashAttention-2 forward: thin Python binding.
+
+The compute lives entirely in ``libfa_fwd.so`` (HIP kernels behind the C ABI
+declared in ``include/fa.h``).  This module only marshals arguments: raw
+device pointers, sizes and a stream handle.  PyTorch is used, when the
+caller passes tensors, for device memory and streams only.
+
+There is no fallback: if the library is missing, importing the binding's
+entry points raises ``FABuildError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa_fwd.so")
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED_D",
+    4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_ARG", 7: "FA_ERR_LAUNCH",
+}
+# every function the C header declares
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_abi_version",
+           "fa_tile_config")
+
+
+class FABuildError(RuntimeError):
+    pass
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa_fwd.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FABuildError(
+            f"{path} is missing: build it with `python -m "
+            "exact_io_aware_08_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd.argtypes = sig
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = sig
+    lib.fa_fwd_f32.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    lib.fa_tile_config.argtypes = [i, i, ctypes.POINTER(i), ctypes.POINTER(i),
+                                   ctypes.POINTER(i)]
+    lib.fa_tile_config.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    raise TypeError(f"expected a device pointer or tensor, got {type(x)!r}")
+
+
+def _stream(s) -> int:
+    if s is None:
+        return 0
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return int(s.cuda_stream)
+    raise TypeError(f"expected a stream handle, got {type(s)!r}")
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load_library().fa_abi_version())
+
+
+def tile_config(dtype: str, d: int):
+    """(block_m, block_n, threads) the library uses for dtype 'bf16'/'fp32'."""
+    lib = load_library()
+    bm, bn, th = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    st = lib.fa_tile_config(0 if dtype == "bf16" else 1, int(d),
+                            ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(th))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return bm.value, bn.value, th.value
+
+
+def _call(fn, q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream):
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+            int(Lq), int(Lk), int(d), int(causal), float(scale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
+
+
+def fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream=None):
+    """bf16 forward through the C ABI (``fa_fwd`` in include/fa.h).
+
+    q, k, v, o, lse: device pointers (ints) or tensors; stream: hipStream_t
+    handle, a torch stream, or None for the null stream.  Raises FAError on
+    a nonzero status."""
+    return _call(load_library().fa_fwd, q, k, v, o, lse, B, H, Lq, Lk, d,
+                 causal, scale, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream=None):
+    """fp32 forward through the C ABI (``fa_fwd_f32``)."""
+    return _call(load_library().fa_fwd_f32, q, k, v, o, lse, B, H, Lq, Lk, d,
+                 causal, scale, stream)
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None,
+              stream=None):
+    """Convenience wrapper on torch tensors [B,H,L,d] (bf16 or fp32, on the
+    GPU, contiguous): allocates O and LSE with torch and calls the C ABI on
+    ``stream`` (default: torch's current stream).  Returns (O, LSE)."""
+    import torch
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, L, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
+        raise ValueError("k and v must be [B, H, Lk, d] matching q")
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if q.dtype == torch.bfloat16:
+        fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
+    elif q.dtype == torch.float32:
+        fa_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return o, lse
+
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "attention", "status_string",
+           "abi_version", "tile_config", "load_library", "FAError",
+           "FABuildError", "EXPORTS", "LIB_PATH"]

@@ -1,0 +1,108 @@
+// C-ABI entry points of libfa_fwd.so (declared in include/fa.h).
+//
+// Every argument check runs here, on the host, before any HIP call: a
+// nonzero status means nothing was enqueued.  The only HIP calls are the
+// kernel launch and hipGetLastError right after it.
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) {
+    return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0;
+}
+
+// [p, p + bytes) overlaps [r, r + rbytes)
+bool overlaps(const void* p, std::size_t bytes, const void* r, std::size_t rbytes) {
+    const auto a = reinterpret_cast<std::uintptr_t>(p);
+    const auto b = reinterpret_cast<std::uintptr_t>(r);
+    return a < b + rbytes && b < a + bytes;
+}
+
+int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
+                        const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Lq, int Lk, int d, int causal,
+                        float scale, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+    fa::TileConfig tc;
+    if (!fa::tile_config(dt, d, &tc)) return FA_ERR_UNSUPPORTED_D;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+        !aligned16(lse))
+        return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+
+    // sizes: element counts must fit the kernel's 64-bit offsets and the
+    // per-head int arithmetic; the grid must fit one dimension.
+    const long long bh = (long long)B * H;
+    const long long nqb = ((long long)Lq + tc.block_m - 1) / tc.block_m;
+    const long long grid = nqb * bh;
+    if (bh > (1LL << 30) || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)Lq * d > 0x7fffffffLL || (long long)Lk * d > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
+    const std::size_t qbytes = (std::size_t)bh * Lq * d * esize;
+    const std::size_t kbytes = (std::size_t)bh * Lk * d * esize;
+    const std::size_t lbytes = (std::size_t)bh * Lq * sizeof(float);
+    if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) ||
+        overlaps(o, qbytes, v, kbytes) || overlaps(lse, lbytes, q, qbytes) ||
+        overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
+        overlaps(lse, lbytes, o, qbytes))
+        return FA_ERR_ARG;
+
+    const hipError_t err = fa::launch_fwd(dt, q, k, v, o, lse, B, H, Lq, Lk, d,
+                                          causal == 1, scale, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Lq, int Lk, int d, int causal, float scale,
+           hipStream_t stream) {
+    return validate_and_launch(fa::DType::BF16, 2, q, k, v, o, lse, B, H, Lq,
+                               Lk, d, causal, scale, stream);
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int Lq, int Lk, int d, int causal,
+               float scale, hipStream_t stream) {
+    return validate_and_launch(fa::DType::F32, 4, q, k, v, o, lse, B, H, Lq,
+                               Lk, d, causal, scale, stream);
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "B, H, Lq and Lk must be >= 1 and sizes must fit";
+    case FA_ERR_UNSUPPORTED_D: return "head dim d must be 64, 128 or 256";
+    case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ARG: return "causal must be 0 or 1 and outputs must not overlap inputs";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+int fa_tile_config(int dtype, int d, int* block_m, int* block_n, int* threads) {
+    if (dtype != 0 && dtype != 1) return FA_ERR_ARG;
+    fa::TileConfig tc;
+    if (!fa::tile_config(dtype == 0 ? fa::DType::BF16 : fa::DType::F32, d, &tc))
+        return FA_ERR_UNSUPPORTED_D;
+    if (block_m) *block_m = tc.block_m;
+    if (block_n) *block_n = tc.block_n;
+    if (threads) *threads = tc.threads;
+    return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,481 @@
+// FlashAttention-2 forward kernel for gfx950 (MI355X, CDNA4).
+//
+// Computes O = softmax(Q K^T * scale) V and LSE = ln(sum_j exp(s_ij)) for
+// each (batch, head, query row), streaming K/V tiles through LDS with the
+// online-softmax update so the score matrix never leaves the chip.
+//
+// Method (the pages' schedule, re-derived for CDNA4):
+//  * one workgroup per (query block, batch*head) with Q resident on chip
+//    and K/V streamed in tiles ("從零開始用自定義 Triton 內核編寫
+//    FlashAttention-2" (digipub.cc), sections "程序網格和並行化策略" and
+//    "K 和 V 塊的流式循環");
+//  * per tile: S = Q K^T * scale, running max m, P = exp(S - m),
+//    alpha = exp(m_old - m), l = l*alpha + rowsum P, O = O*alpha + P V
+//    ("第 08 章: Flash Attention——分块注意力" (chuoer47.github.io),
+//    section 2 "在线 softmax", steps 1-7), in base 2 with scale * log2(e)
+//    folded in (same page, section 1 "tl.exp2");
+//  * O / l once after the last tile and LSE = m + log l (same page,
+//    sections 2 and 3);
+//  * causal: tiles right of the diagonal are never visited, tiles that
+//    straddle it are masked element-wise (same page, section 4).
+//
+// gfx950 mapping (not the pages' Triton tiling):
+//  * each wave owns 32*NBQ query rows; 4 waves share one K/V tile in LDS;
+//  * both products use v_mfma_f32_32x32x16_bf16 (fp32: 32x32x2f32) in the
+//    transposed form S^T = K Q^T and O^T = V^T P^T.  In that form every
+//    lane's accumulator column is one query, so the row max/sum are
+//    in-lane plus one exchange between the two 32-lane halves, alpha
+//    scales a lane's own O values, and the S^T accumulator registers are
+//    already the P^T operand of the next MFMA (no LDS round trip for P);
+//  * K rows are stored in LDS in a permuted order so that lane half h's
+//    accumulator rows are the 16 consecutive keys 16h..16h+15 of each
+//    32-key block; V is stored transposed (V^T, keys contiguous) so each
+//    P^T V^T operand is one 16-byte LDS read;
+//  * K/V tiles are double-buffered: tile j+1 is fetched from HBM into
+//    registers while tile j is computed, then written to the other buffer;
+//  * workgroup ids are remapped so that all query blocks of a head run on
+//    one XCD (its L2 serves the K/V re-reads) and, for causal, the
+//    heaviest query blocks start first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T, int N> struct VecOf {
+    typedef T type __attribute__((ext_vector_type(N)));
+};
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
+constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// ---- element traits -------------------------------------------------------
+
+struct BF16 {
+    using T = uint16_t;   // storage: raw bfloat16 bits
+    using Frag = bf16x8;  // one MFMA A/B operand per lane
+    static constexpr int KPL = 8;   // contraction elements per lane per MFMA
+    static constexpr int VEC = 8;   // elements per 16-byte global chunk
+    __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline Frag load(const T* p) {
+        return *reinterpret_cast<const bf16x8*>(p);
+    }
+    // fp32 probabilities -> operand (round to nearest even)
+    __device__ static inline Frag from_f32(const float* x) {
+        f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+        return __builtin_convertvector(v, bf16x8);
+    }
+    __device__ static inline void store4(T* dst, f32x4 v) {
+        bf16x4 b = __builtin_convertvector(v, bf16x4);
+        *reinterpret_cast<bf16x4*>(dst) = b;
+    }
+};
+
+struct F32 {
+    using T = float;
+    using Frag = float;
+    static constexpr int KPL = 1;
+    static constexpr int VEC = 4;
+    __device__ static inline f32x16 mfma(Frag a, Frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline Frag load(const T* p) { return *p; }
+    __device__ static inline Frag from_f32(const float* x) { return x[0]; }
+    __device__ static inline void store4(T* dst, f32x4 v) {
+        *reinterpret_cast<f32x4*>(dst) = v;
+    }
+};
+
+// ---- per-(dtype, d) tile table -------------------------------------------
+
+template <class E, int D> struct Cfg;
+template <> struct Cfg<BF16, 64>  { static constexpr int NBQ = 2, BN = 64; };
+template <> struct Cfg<BF16, 128> { static constexpr int NBQ = 2, BN = 64; };
+template <> struct Cfg<BF16, 256> { static constexpr int NBQ = 1, BN = 64; };
+template <> struct Cfg<F32, 64>   { static constexpr int NBQ = 1, BN = 32; };
+template <> struct Cfg<F32, 128>  { static constexpr int NBQ = 1, BN = 32; };
+template <> struct Cfg<F32, 256>  { static constexpr int NBQ = 1, BN = 32; };
+
+template <class E, int D> struct Geom {
+    using T = typename E::T;
+    static constexpr int NBQ = Cfg<E, D>::NBQ;   // 32-query blocks per wave
+    static constexpr int BN = Cfg<E, D>::BN;     // keys per tile
+    static constexpr int BM = kWaves * 32 * NBQ; // query rows per workgroup
+    static constexpr int KPL = E::KPL;
+    static constexpr int KSTEP = 2 * KPL;        // contraction per MFMA
+    static constexpr int NS = D / KSTEP;         // MFMAs along d for S
+    static constexpr int NMB = BN / 32;          // 32-key blocks per tile
+    static constexpr int NDB = D / 32;           // 32-wide d blocks of O
+    static constexpr int NPV = 32 / KSTEP;       // PV MFMAs per key block
+    static constexpr int VEC = E::VEC;
+    // LDS rows padded by one 16-byte chunk
+    static constexpr int KS = D + VEC;           // K row stride (elements)
+    static constexpr int VS = BN + VEC;          // V^T row stride (elements)
+    static constexpr int K_ELEMS = BN * KS;
+    static constexpr int V_ELEMS = D * VS;
+    static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
+    static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * (int)sizeof(T);
+    // cooperative loads: 16-byte chunks per thread per tensor per tile
+    static constexpr int CH = BN * D / VEC / kThreads;
+    static constexpr int NKG = BN / CH;          // V key groups (CH keys each)
+    static_assert(CH >= 1 && CH * kThreads * VEC == BN * D, "tile/threads");
+    static_assert(NKG * (D / VEC) == kThreads, "V transpose mapping");
+    static_assert(D % KSTEP == 0 && BN % 32 == 0 && D % 32 == 0, "shape");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+// Slot of key k (0..31) inside a 32-row block of the K tile in LDS.  MFMA
+// A-operand row r is read by lane r; its accumulator row r sits in lane
+// half (r>>2)&1 at index 4*(r>>3)+(r&3).  Storing key
+// 16*((r>>2)&1) + 4*(r>>3) + (r&3) in slot r makes accumulator index i of
+// lane half h hold key 16*h + i.  This is the inverse of that map.
+__device__ inline int k_slot(int k) {
+    return 8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3);
+}
+
+template <class E, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_fwd_kernel(const typename E::T* __restrict__ Q,
+                   const typename E::T* __restrict__ K,
+                   const typename E::T* __restrict__ V,
+                   typename E::T* __restrict__ O, float* __restrict__ LSE,
+                   int BH, int Lq, int Lk, int nqb, float c)
+{
+    using G = Geom<E, D>;
+    using T = typename G::T;
+    using Frag = typename E::Frag;
+    constexpr int NBQ = G::NBQ, BN = G::BN, BM = G::BM, KPL = G::KPL;
+    constexpr int KSTEP = G::KSTEP, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
+    constexpr int NPV = G::NPV, VEC = G::VEC, KS = G::KS, VS = G::VS;
+    constexpr int CH = G::CH, NKG = G::NKG;
+
+    __shared__ __attribute__((aligned(16))) T smem[2 * G::STAGE_ELEMS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;   // accumulator column = query
+    const int half = lane >> 5;  // lane half
+
+    // ---- work decode: XCD-grouped heads, heaviest causal blocks first ----
+    int bh, lvl;
+    {
+        const int p = blockIdx.x;
+        if ((BH & 7) == 0) {
+            const int own = BH >> 3;          // heads per XCD
+            const int slot = p >> 3;
+            bh = (p & 7) + 8 * (slot % own);
+            lvl = slot / own;
+        } else {
+            bh = p % BH;
+            lvl = p / BH;
+        }
+    }
+    const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
+    const int q0 = qb * BM;
+    const int q0w = q0 + wave * 32 * NBQ;          // first row of this wave
+    const int qlast_w = q0w + 32 * NBQ - 1;        // last row of this wave
+
+    const T* Qh = Q + (size_t)bh * Lq * D;
+    const T* Kh = K + (size_t)bh * Lk * D;
+    const T* Vh = V + (size_t)bh * Lk * D;
+
+    // ---- Q fragments: resident for the whole key loop --------------------
+    Frag qf[NBQ][NS];
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const int row = q0w + nb * 32 + col;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            if (row < Lq) {
+                qf[nb][s] = E::load(Qh + (size_t)row * D + s * KSTEP + half * KPL);
+            } else {
+                qf[nb][s] = Frag{};
+            }
+        }
+    }
+
+    f32x16 oacc[NDB][NBQ];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) oacc[db][nb] = f32x16{};
+    float m_run[NBQ], l_run[NBQ];
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        m_run[nb] = -__builtin_inff();
+        l_run[nb] = 0.f;
+    }
+
+    const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
+    const int nt = (kv_end + BN - 1) / BN;
+
+    // ---- cooperative tile movement ---------------------------------------
+    u32x4 kreg[CH], vreg[CH];
+    auto load_tile = [&](int j) {
+        const int kv0 = j * BN;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int cidx = tid + kThreads * i;
+            const int row = cidx / (D / VEC);
+            const int cc = cidx % (D / VEC);
+            if (kv0 + row < Lk)
+                kreg[i] = *reinterpret_cast<const u32x4*>(Kh + (size_t)(kv0 + row) * D + cc * VEC);
+            else
+                kreg[i] = u32x4{};
+        }
+        const int kg = tid % NKG, dc = tid / NKG;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int row = kg * CH + i;
+            if (kv0 + row < Lk)
+                vreg[i] = *reinterpret_cast<const u32x4*>(Vh + (size_t)(kv0 + row) * D + dc * VEC);
+            else
+                vreg[i] = u32x4{};
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* Ks = smem + buf * G::STAGE_ELEMS;
+        T* Vt = Ks + G::K_ELEMS;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int cidx = tid + kThreads * i;
+            const int row = cidx / (D / VEC);
+            const int cc = cidx % (D / VEC);
+            const int slot = (row & ~31) | k_slot(row & 31);
+            *reinterpret_cast<u32x4*>(Ks + slot * KS + cc * VEC) = kreg[i];
+        }
+        // V^T: thread holds CH consecutive keys x VEC consecutive d; write
+        // one row segment of CH keys per d (at most 16 bytes per store).
+        const int kg = tid % NKG, dc = tid / NKG;
+        using Chunk = typename VecOf<T, VEC>::type;
+        constexpr int SEG = (CH * (int)sizeof(T) >= 16) ? VEC : CH;
+        using Seg = typename VecOf<T, SEG>::type;
+        Chunk rows[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) rows[i] = __builtin_bit_cast(Chunk, vreg[i]);
+#pragma unroll
+        for (int dd = 0; dd < VEC; ++dd) {
+            T* dst = Vt + (dc * VEC + dd) * VS + kg * CH;
+#pragma unroll
+            for (int p0 = 0; p0 < CH; p0 += SEG) {
+                Seg sv;
+#pragma unroll
+                for (int e = 0; e < SEG; ++e) sv[e] = rows[p0 + e][dd];
+                *reinterpret_cast<Seg*>(dst + p0) = sv;
+            }
+        }
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < nt; ++j) {
+        const int buf = j & 1;
+        const int kv0 = j * BN;
+        if (j + 1 < nt) load_tile(j + 1);
+
+        // waves whose rows all precede this tile's first key skip it
+        const bool active = !CAUSAL || kv0 <= qlast_w;
+        if (active) {
+            const T* Ks = smem + buf * G::STAGE_ELEMS;
+            const T* Vt = Ks + G::K_ELEMS;
+
+            // S^T = K Q^T: rows = keys (permuted slots), columns = queries
+            f32x16 sacc[NMB][NBQ];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NBQ; ++nb) sacc[mb][nb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    const Frag a = E::load(Ks + (mb * 32 + col) * KS + s * KSTEP + half * KPL);
+#pragma unroll
+                    for (int nb = 0; nb < NBQ; ++nb)
+                        sacc[mb][nb] = E::mfma(a, qf[nb][s], sacc[mb][nb]);
+                }
+            }
+
+            // mask: keys beyond Lk, and keys after the query (causal)
+            const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0w);
+            if (need_mask) {
+#pragma unroll
+                for (int nb = 0; nb < NBQ; ++nb) {
+                    const int qi = q0w + nb * 32 + col;
+#pragma unroll
+                    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int kj = kv0 + mb * 32 + 16 * half + i;
+                            const bool dead = (kj >= Lk) || (CAUSAL && kj > qi);
+                            if (dead) sacc[mb][nb][i] = -__builtin_inff();
+                        }
+                }
+            }
+
+            // online softmax (base 2), per query column
+            Frag pf[NMB][NPV][NBQ];
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][nb][i]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float m_new = fmaxf(m_run[nb], mx * c);
+                // a row with no visible key yet keeps alpha = 1, P = 0
+                const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
+                float rs = 0.f;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb) {
+                    float p[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][nb][i], c, -m_use));
+                        rs += p[i];
+                    }
+#pragma unroll
+                    for (int t = 0; t < NPV; ++t) pf[mb][t][nb] = E::from_f32(p + t * KPL);
+                }
+                l_run[nb] = l_run[nb] * alpha + rs;
+                m_run[nb] = m_new;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db][nb] *= alpha;
+            }
+
+            // O^T += V^T P^T: rows = d, columns = queries
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int t = 0; t < NPV; ++t)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const Frag a = E::load(Vt + (db * 32 + col) * VS + mb * 32 + 16 * half + t * KPL);
+#pragma unroll
+                        for (int nb = 0; nb < NBQ; ++nb)
+                            oacc[db][nb] = E::mfma(a, pf[mb][t][nb], oacc[db][nb]);
+                    }
+        }
+
+        if (j + 1 < nt) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O / l, LSE = ln2 * (m + log2 l) -------------------------
+    T* Oh = O + (size_t)bh * Lq * D;
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
+        const float inv = 1.0f / lt;
+        const int row = q0w + nb * 32 + col;
+        if (row < Lq) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v4 = {oacc[db][nb][4 * g + 0], oacc[db][nb][4 * g + 1],
+                                oacc[db][nb][4 * g + 2], oacc[db][nb][4 * g + 3]};
+                    v4 *= inv;
+                    E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
+                }
+            if (half == 0)
+                LSE[(size_t)bh * Lq + row] = (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
+    }
+}
+
+template <class E, int D, bool CAUSAL>
+hipError_t launch_one(const void* q, const void* k, const void* v, void* o,
+                      float* lse, int B, int H, int Lq, int Lk, float scale,
+                      hipStream_t stream)
+{
+    using G = Geom<E, D>;
+    using T = typename E::T;
+    const int BH = B * H;
+    const int nqb = (Lq + G::BM - 1) / G::BM;
+    const long long nblocks = (long long)nqb * BH;
+    const float c = scale * kLog2e;
+    hipLaunchKernelGGL((fa_fwd_kernel<E, D, CAUSAL>), dim3((unsigned)nblocks),
+                       dim3(kThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), static_cast<T*>(o), lse,
+                       BH, Lq, Lk, nqb, c);
+    return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int Lq, int Lk, bool causal,
+                    float scale, hipStream_t stream)
+{
+    return causal ? launch_one<E, D, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
+                  : launch_one<E, D, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
+}
+
+template <class E>
+hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int B, int H, int Lq, int Lk, int d,
+                    bool causal, float scale, hipStream_t stream)
+{
+    switch (d) {
+    case 64:  return launch_d<E, 64>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    case 128: return launch_d<E, 128>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    case 256: return launch_d<E, 256>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    default:  return hipErrorInvalidValue;
+    }
+}
+
+template <class E, int D>
+TileConfig cfg_of() {
+    return TileConfig{Geom<E, D>::BM, Geom<E, D>::BN, kThreads};
+}
+
+}  // namespace
+
+bool tile_config(DType dt, int d, TileConfig* out)
+{
+    if (dt == DType::BF16) {
+        switch (d) {
+        case 64:  *out = cfg_of<BF16, 64>();  return true;
+        case 128: *out = cfg_of<BF16, 128>(); return true;
+        case 256: *out = cfg_of<BF16, 256>(); return true;
+        }
+    } else if (dt == DType::F32) {
+        switch (d) {
+        case 64:  *out = cfg_of<F32, 64>();  return true;
+        case 128: *out = cfg_of<F32, 128>(); return true;
+        case 256: *out = cfg_of<F32, 256>(); return true;
+        }
+    }
+    return false;
+}
+
+hipError_t launch_fwd(DType dt, const void* q, const void* k, const void* v,
+                      void* o, float* lse, int B, int H, int Lq, int Lk,
+                      int d, bool causal, float scale, hipStream_t stream)
+{
+    if (dt == DType::BF16)
+        return launch_e<BF16>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
+    return launch_e<F32>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,27 @@
+// Internal interface between the C-ABI shim (fa_api.cpp) and the kernel
+// translation unit (fa_fwd_kernel.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace fa {
+
+enum class DType { BF16 = 0, F32 = 1 };
+
+// Tile geometry of one compiled instantiation.
+struct TileConfig {
+    int block_m;   // query rows per workgroup
+    int block_n;   // keys per K/V tile
+    int threads;   // threads per workgroup
+};
+
+// Geometry for (dtype, d); returns false if no instantiation exists.
+bool tile_config(DType dt, int d, TileConfig* out);
+
+// Enqueue the forward kernel.  Arguments were validated by the caller.
+// Returns the hipError_t of the launch.
+hipError_t launch_fwd(DType dt, const void* q, const void* k, const void* v,
+                      void* o, float* lse, int B, int H, int Lq, int Lk,
+                      int d, bool causal, float scale, hipStream_t stream);
+
+}  // namespace fa

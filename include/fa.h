@@ -1,0 +1,106 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) FlashAttention-2 forward library
+ *        (libfa_fwd.so).
+ *
+ * Operation (both entry points):  for every batch b < B, head h < H and
+ * query row i < Lq,
+ *
+ *     s_ij   = scale * sum_t q[b,h,i,t] * k[b,h,j,t]        j < Lk
+ *     A_i    = { j < Lk }                  (causal == 0)
+ *            = { j < Lk : j <= i }         (causal == 1, top-left aligned)
+ *     o[b,h,i,:] = sum_{j in A_i} softmax_j(s_i.) * v[b,h,j,:]
+ *     lse[b,h,i] = ln( sum_{j in A_i} exp(s_ij) )           natural log
+ *
+ * i.e. O = softmax(Q K^T * scale) V plus the per-row log-sum-exp, the
+ * exact scaled dot-product attention result ("Flash Attention 原理与实现详解：
+ * 如何通过 IO-Aware 算法突破注意力机制的计算瓶颈" (tbr8.org), section 一 and
+ * section 3 "Flash Attention v2"; the LSE output of "第 08 章: Flash
+ * Attention——分块注意力" (chuoer47.github.io), section 3 "LSE"; the causal
+ * lower triangle including the diagonal, same page, section 4).  It is
+ * computed tile by tile with the online-softmax update ("從零開始用自定義
+ * Triton 內核編寫 FlashAttention-2" (digipub.cc), sections "流式注意力內核
+ * _attn_fwd_inner" and "部分分數計算和在線更新"), so the Lq x Lk score matrix
+ * never reaches device memory.
+ *
+ * Layout: q and o are [B, H, Lq, d], k and v are [B, H, Lk, d], all dense
+ * row-major (d fastest) with no padding; lse is [B, H, Lq] fp32.  All five
+ * are device pointers, 16-byte aligned.
+ *
+ * Ownership: the caller owns every buffer.  The library never allocates,
+ * frees or synchronises; each call enqueues exactly one kernel on `stream`
+ * (a hipStream_t; 0 means the null stream) and returns.  o and lse must not
+ * overlap q, k, v or each other.  Calls are thread-safe (no global mutable
+ * state).
+ *
+ * Errors: every argument check runs on the host before any HIP call; on a
+ * nonzero return nothing was enqueued.  FA_ERR_LAUNCH reports a failed
+ * launch (hipGetLastError after the launch).  Faults during execution
+ * surface at the caller's next synchronisation of `stream`.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,           /* a pointer argument is NULL                 */
+    FA_ERR_SHAPE = 2,          /* B, H, Lq or Lk < 1, or a size overflows    */
+    FA_ERR_UNSUPPORTED_D = 3,  /* d is not 64, 128 or 256                    */
+    FA_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned           */
+    FA_ERR_SCALE = 5,          /* scale is not finite and > 0                */
+    FA_ERR_ARG = 6,            /* causal not 0/1, or outputs overlap inputs  */
+    FA_ERR_LAUNCH = 7          /* the kernel launch failed                   */
+};
+
+/*
+ * bf16 forward (the benchmarked entry point).  q, k, v, o hold bfloat16
+ * values (raw 16-bit patterns); lse is fp32.  Products QK^T and PV run on
+ * bf16 MFMA with fp32 accumulation; P is rounded to bf16 (round to nearest
+ * even) before the PV product, as the pages cast P to V's dtype
+ * ("FlashAttention的Triton实现：IO-aware注意力机制底层原理" (gitcode.csdn.net),
+ * section "FlashAttention的Triton Kernel结构"); o is rounded to bf16 with
+ * round to nearest even.
+ *   d      : 64, 128 or 256
+ *   causal : 0 (all keys) or 1 (key j visible to query i iff j <= i)
+ *   scale  : multiplies QK^T; finite and > 0 (usually 1/sqrt(d))
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int Lq, int Lk, int d, int causal, float scale,
+           hipStream_t stream);
+
+/*
+ * fp32 forward: q, k, v, o are fp32; the same kernel template on the fp32
+ * MFMA (P stays fp32).  Same arguments, layout, ownership and errors as
+ * fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
+               float* lse, int B, int H, int Lq, int Lk, int d, int causal,
+               float scale, hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/*
+ * Tile geometry the library uses for (dtype, d): query rows per workgroup
+ * (block_m), keys per K/V tile (block_n) and threads per workgroup.  dtype
+ * is 0 for bf16, 1 for fp32.  Returns FA_OK, or FA_ERR_UNSUPPORTED_D /
+ * FA_ERR_ARG for an unknown combination.  Host-only; makes no HIP call.
+ */
+int fa_tile_config(int dtype, int d, int* block_m, int* block_n,
+                   int* threads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

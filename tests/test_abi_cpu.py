@@ -1,0 +1,96 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol that
+include/fa.h declares, and rejects bad arguments on the host before any HIP
+call (these calls never reach a launch, so no GPU is needed)."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_io_aware_08_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# distinct, 16-byte aligned fake device addresses: never dereferenced,
+# because every call below fails validation first
+Q, K, V, O, L = (0x10000000 * i for i in range(1, 6))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_header_declares_expected_symbols():
+    assert declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+FA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert fa.abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for st in range(8):
+        assert fa.status_string(st)
+    assert fa.status_string(99) == "unknown status"
+
+
+def test_tile_config():
+    for dt in ("bf16", "fp32"):
+        for d in (64, 128, 256):
+            bm, bn, th = fa.tile_config(dt, d)
+            assert bm % 32 == 0 and bn % 32 == 0 and th == 256
+    with pytest.raises(fa.FAError):
+        fa.tile_config("bf16", 96)
+
+
+def _st(fn, **kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Lq=128, Lk=128, d=64,
+                causal=0, scale=0.125)
+    args.update(kw)
+    try:
+        fn(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+@pytest.mark.parametrize("fn", [fa.fa_fwd, fa.fa_fwd_f32])
+def test_validation_errors(fn):
+    assert _st(fn, q=0) == 1
+    assert _st(fn, lse=0) == 1
+    for bad in ({"B": 0}, {"H": -1}, {"Lq": 0}, {"Lk": 0}):
+        assert _st(fn, **bad) == 2
+    for d in (0, 32, 96, 512):
+        assert _st(fn, d=d) == 3
+    assert _st(fn, k=K + 8) == 4
+    assert _st(fn, o=O + 2) == 4
+    for s in (0.0, -0.5, math.inf, math.nan):
+        assert _st(fn, scale=s) == 5
+    assert _st(fn, causal=2) == 6
+    assert _st(fn, causal=-1) == 6
+    # outputs overlapping an input or each other
+    assert _st(fn, o=Q + 256) == 6
+    assert _st(fn, lse=V + 1024) == 6
+    assert _st(fn, lse=O + 16) == 6
+    # a grid too large for one dimension
+    assert _st(fn, B=1 << 16, H=1 << 15, Lq=1 << 20) == 2

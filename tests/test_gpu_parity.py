@@ -1,0 +1,179 @@
+"""GPU parity: the HIP forward (through the C ABI) against the fp64 oracle on
+identical seeded inputs, element by element.
+
+Bars: fp32 max|err| / max|ref| <= 1e-5 per tensor; bf16 max-abs error
+<= 2e-2 on O and <= 1e-3 on LSE, against the oracle fed the same
+bf16-rounded inputs.  Small shapes are compared in full (several tiles,
+ragged tails); the five full-size workloads are compared on sampled rows,
+in the launch configuration the bench times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import exact_io_aware_08_amd as fa
+from oracle import attention_ref
+from seeded_inputs import WORKLOADS, make_inputs, widen, workload_inputs
+from tests.gpu_helpers import (check_parity, run_fa, sample_rows, say,
+                               to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def f32_scale(d):
+    return float(np.float32(1.0) / np.sqrt(np.float32(d)))
+
+
+def full_case(seed, B, H, Lq, Lk, d, dtype, causal, sigma_qk=1.0, scale=None):
+    q, k, v = make_inputs(seed, B, H, Lq, Lk, d, dtype, sigma_qk=sigma_qk)
+    scale = f32_scale(d) if scale is None else scale
+    label = f"{dtype} B={B} H={H} Lq={Lq} Lk={Lk} d={d} causal={causal}"
+    say(f"case {label}")
+    O, LSE = run_fa(q, k, v, causal, scale)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), causal, scale,
+                                 workers=8)
+    return check_parity(O, LSE, O_ref, L_ref, dtype, label)
+
+
+# ---- the tiny fp32 workload, both modes, in full -------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_fp32_workload(causal):
+    w = WORKLOADS["tiny_fp32"]
+    full_case(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, "fp32", causal)
+
+
+# the pages' own test shapes (fp32, causal), including the ragged N=69
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 128, 64), (1, 1, 128, 128),
+                                     (32, 8, 69, 128), (1, 2, 100, 256)])
+def test_fp32_page_shapes(B, H, N, d):
+    full_case(21, B, H, N, N, d, "fp32", True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lk,d", [(300, 300, 64), (257, 500, 128),
+                                     (500, 257, 128), (130, 70, 256)])
+def test_fp32_ragged(causal, Lq, Lk, d):
+    full_case(22, 1, 2, Lq, Lk, d, "fp32", causal)
+
+
+# ---- bf16, small shapes in full -----------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,Lq,Lk,d", [
+    (1, 2, 300, 300, 64), (2, 3, 200, 333, 128), (1, 2, 333, 200, 128),
+    (1, 2, 130, 70, 256), (1, 1, 1, 1, 64), (1, 1, 1, 77, 128),
+    (1, 1, 77, 1, 256), (1, 8, 512, 512, 128), (2, 1, 1000, 1000, 256),
+    (1, 1, 69, 69, 128), (3, 5, 96, 160, 64)])
+def test_bf16_small(causal, B, H, Lq, Lk, d):
+    full_case(23, B, H, Lq, Lk, d, "bf16", causal)
+
+
+def test_bf16_peaky_small():
+    # sigma 3 on Q, K: large logits exercise the rescaling and tail masks
+    full_case(24, 1, 2, 400, 520, 256, "bf16", False, sigma_qk=3.0)
+    full_case(25, 1, 2, 400, 520, 128, "bf16", True, sigma_qk=3.0)
+
+
+# ---- the bf16 causal 1k workload, in full --------------------------------
+
+def test_bf16_causal_1k_workload_full():
+    w = WORKLOADS["bf16_causal_1k_d64"]
+    full_case(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, "bf16", True)
+
+
+# ---- full-size workloads on sampled rows ---------------------------------
+
+def sampled_workload(name, causal, n_random=96):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    label = f"{name} causal={causal}"
+    say(f"case {label} (full size, sampled rows)")
+    O, LSE = run_fa(q, k, v, causal, w.scale)
+    bm, _, _ = fa.tile_config(w.dtype, w.d)
+    rows = sample_rows(w.Lq, bm, n_random, w.seed)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), causal, w.scale,
+                                 rows=rows, workers=8, chunk=64)
+    check_parity(O[:, :, rows], LSE[:, :, rows], O_ref, L_ref, w.dtype, label)
+    # every row, not only the sampled ones, must be finite
+    assert np.isfinite(widen(O)).all() and np.isfinite(LSE).all()
+    return O, LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_4k_d128_workload_sampled(causal):
+    sampled_workload("bf16_4k_d128", causal)
+
+
+def test_bf16_causal_16k_workload_sampled():
+    sampled_workload("bf16_causal_16k_d128", True)
+
+
+def test_bf16_peaky_d256_ragged_workload_sampled():
+    sampled_workload("bf16_peaky_d256_ragged", False)
+
+
+# ---- closed forms and metamorphic checks ---------------------------------
+
+def test_causal_row0_equals_v0_bitwise():
+    q, k, v = make_inputs(31, 2, 4, 300, 300, 128, "bf16")
+    scale = f32_scale(128)
+    O, LSE = run_fa(q, k, v, True, scale)
+    np.testing.assert_array_equal(O[:, :, 0], v[:, :, 0])
+    lse0 = scale * (widen(q)[:, :, 0] * widen(k)[:, :, 0]).sum(-1)
+    assert np.abs(LSE[:, :, 0] - lse0).max() <= 1e-3
+
+
+def test_tiny_scale_gives_means():
+    q, k, v = make_inputs(32, 1, 2, 200, 333, 64, "bf16")
+    O, LSE = run_fa(q, k, v, False, 1e-30)
+    mean = widen(v).mean(axis=2, keepdims=True)
+    assert np.abs(widen(O) - mean).max() <= 2e-2
+    assert np.abs(LSE - math.log(333)).max() <= 1e-3
+    Oc, Lc = run_fa(q, k, v, True, 1e-30)
+    prefix = np.cumsum(widen(v), axis=2)[:, :, :200] / np.arange(1, 201)[:, None]
+    assert np.abs(widen(Oc) - prefix).max() <= 2e-2
+    assert np.abs(Lc - np.log(np.arange(1, 201))).max() <= 1e-3
+
+
+def test_key_shift_metamorphic():
+    # K on a 1/16 grid with |K| < 8 and a shift u on the same grid keep
+    # K + u exact in bf16; then O is unchanged and LSE moves by scale*q.u
+    from seeded_inputs import round_to_bf16_bits
+    rng = np.random.default_rng(33)
+    B, H, L, d = 1, 2, 320, 128
+    q, _, v = make_inputs(33, B, H, L, L, d, "bf16")
+    kf = np.clip(np.round(16 * rng.standard_normal((B, H, L, d))) / 16, -7.9375, 7.9375)
+    u = np.round(16 * rng.uniform(-4, 4, d)) / 16
+    k1 = round_to_bf16_bits(kf.astype(np.float32))
+    k2 = round_to_bf16_bits((kf + u).astype(np.float32))
+    assert (widen(k2) == kf + u).all() and (widen(k1) == kf).all()
+    scale = f32_scale(d)
+    for causal in (False, True):
+        O1, L1 = run_fa(q, k1, v, causal, scale)
+        O2, L2 = run_fa(q, k2, v, causal, scale)
+        assert np.abs(widen(O1) - widen(O2)).max() <= 2e-2
+        shift = scale * (widen(q) @ u)
+        assert np.abs((L2 - L1) - shift).max() <= 2e-3
+
+
+def test_deterministic_and_stream():
+    import torch
+    q, k, v = make_inputs(34, 1, 4, 700, 700, 128, "bf16")
+    O1, L1 = run_fa(q, k, v, True, f32_scale(128))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        O2, L2 = run_fa(q, k, v, True, f32_scale(128), stream=s)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
+
+
+def test_attention_wrapper_matches_abi():
+    import torch
+    q, k, v = make_inputs(35, 1, 2, 256, 256, 64, "bf16")
+    O, L = run_fa(q, k, v, True, f32_scale(64))
+    o2, l2 = fa.attention(to_device(q), to_device(k), to_device(v), causal=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o2.view(torch.int16).cpu().numpy().view(np.uint16), O)
+    np.testing.assert_array_equal(l2.cpu().numpy(), L)
