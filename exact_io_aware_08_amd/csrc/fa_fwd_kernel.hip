@@ -20,7 +20,8 @@
 //    straddle it are masked element-wise (same page, section 4).
 //
 // gfx950 mapping (not the pages' Triton tiling):
-//  * each wave owns 32*NBQ query rows; 4 waves share one K/V tile in LDS;
+//  * each wave owns 32*NBQ query rows; the NW waves of a workgroup share
+//    one K/V tile in LDS;
 //  * both products use v_mfma_f32_32x32x16_bf16 (fp32: 32x32x2f32) in the
 //    transposed form S^T = K Q^T and O^T = V^T P^T.  In that form every
 //    lane's accumulator column is one query, so the row max/sum are
@@ -58,8 +59,6 @@ template <class T, int N> struct VecOf {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
 constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
 // ---- element traits -------------------------------------------------------
 
@@ -101,20 +100,43 @@ struct F32 {
 };
 
 // ---- per-(dtype, d) tile table -------------------------------------------
+// NBQ: 32-query blocks per wave; BN: keys per K/V tile; NW: waves per
+// workgroup; WPE: waves per SIMD the register budget is sized for (2 lets
+// one wave's softmax overlap another's MFMAs; each wave then has at most
+// 256 registers, all of them architectural VGPRs).
 
+#ifndef FA_CFG_BF16_64
+#define FA_CFG_BF16_64 1, 128, 8, 2
+#endif
+#ifndef FA_CFG_BF16_128
+#define FA_CFG_BF16_128 1, 128, 8, 2
+#endif
+#ifndef FA_CFG_BF16_256
+#define FA_CFG_BF16_256 1, 64, 4, 1
+#endif
+#ifndef FA_CFG_F32
+#define FA_CFG_F32 1, 32, 4, 1
+#endif
+
+template <int NBQ_, int BN_, int NW_, int WPE_> struct CfgT {
+    static constexpr int NBQ = NBQ_, BN = BN_, NW = NW_, WPE = WPE_;
+};
 template <class E, int D> struct Cfg;
-template <> struct Cfg<BF16, 64>  { static constexpr int NBQ = 2, BN = 64; };
-template <> struct Cfg<BF16, 128> { static constexpr int NBQ = 2, BN = 64; };
-template <> struct Cfg<BF16, 256> { static constexpr int NBQ = 1, BN = 64; };
-template <> struct Cfg<F32, 64>   { static constexpr int NBQ = 1, BN = 32; };
-template <> struct Cfg<F32, 128>  { static constexpr int NBQ = 1, BN = 32; };
-template <> struct Cfg<F32, 256>  { static constexpr int NBQ = 1, BN = 32; };
+template <> struct Cfg<BF16, 64>  : CfgT<FA_CFG_BF16_64> {};
+template <> struct Cfg<BF16, 128> : CfgT<FA_CFG_BF16_128> {};
+template <> struct Cfg<BF16, 256> : CfgT<FA_CFG_BF16_256> {};
+template <> struct Cfg<F32, 64>   : CfgT<FA_CFG_F32> {};
+template <> struct Cfg<F32, 128>  : CfgT<FA_CFG_F32> {};
+template <> struct Cfg<F32, 256>  : CfgT<FA_CFG_F32> {};
 
 template <class E, int D> struct Geom {
     using T = typename E::T;
     static constexpr int NBQ = Cfg<E, D>::NBQ;   // 32-query blocks per wave
     static constexpr int BN = Cfg<E, D>::BN;     // keys per tile
-    static constexpr int BM = kWaves * 32 * NBQ; // query rows per workgroup
+    static constexpr int NW = Cfg<E, D>::NW;     // waves per workgroup
+    static constexpr int WPE = Cfg<E, D>::WPE;   // waves per SIMD (target)
+    static constexpr int NT = 64 * NW;           // threads per workgroup
+    static constexpr int BM = NW * 32 * NBQ;     // query rows per workgroup
     static constexpr int KPL = E::KPL;
     static constexpr int KSTEP = 2 * KPL;        // contraction per MFMA
     static constexpr int NS = D / KSTEP;         // MFMAs along d for S
@@ -130,13 +152,32 @@ template <class E, int D> struct Geom {
     static constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
     static constexpr int LDS_BYTES = 2 * STAGE_ELEMS * (int)sizeof(T);
     // cooperative loads: 16-byte chunks per thread per tensor per tile
-    static constexpr int CH = BN * D / VEC / kThreads;
+    static constexpr int CH = BN * D / VEC / NT;
     static constexpr int NKG = BN / CH;          // V key groups (CH keys each)
-    static_assert(CH >= 1 && CH * kThreads * VEC == BN * D, "tile/threads");
-    static_assert(NKG * (D / VEC) == kThreads, "V transpose mapping");
+    static_assert(CH >= 1 && CH * NT * VEC == BN * D, "tile/threads");
+    static_assert(CH * (int)sizeof(T) >= 4, "V^T segments of at least 4 bytes");
+    static_assert(NKG * (D / VEC) == NT, "V transpose mapping");
     static_assert(D % KSTEP == 0 && BN % 32 == 0 && D % 32 == 0, "shape");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(LDS_BYTES * WPE * 4 / NW <= 160 * 1024, "LDS budget");
 };
+
+// Lane l and lane l^32 hold the same query column; combine their values.
+// v_permlane32_swap exchanges the two 32-lane halves without going through
+// the LDS crossbar: each lane receives the value of its partner.
+__device__ inline float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+                 __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) +
+           __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 // Slot of key k (0..31) inside a 32-row block of the K tile in LDS.  MFMA
 // A-operand row r is read by lane r; its accumulator row r sits in lane
@@ -148,7 +189,8 @@ __device__ inline int k_slot(int k) {
 }
 
 template <class E, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((Geom<E, D>::NT))
+__attribute__((amdgpu_waves_per_eu(Geom<E, D>::WPE, Geom<E, D>::WPE)))
 void fa_fwd_kernel(const typename E::T* __restrict__ Q,
                    const typename E::T* __restrict__ K,
                    const typename E::T* __restrict__ V,
@@ -161,7 +203,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
     constexpr int NBQ = G::NBQ, BN = G::BN, BM = G::BM, KPL = G::KPL;
     constexpr int KSTEP = G::KSTEP, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
     constexpr int NPV = G::NPV, VEC = G::VEC, KS = G::KS, VS = G::VS;
-    constexpr int CH = G::CH, NKG = G::NKG;
+    constexpr int CH = G::CH, NKG = G::NKG, NT = G::NT;
 
     __shared__ __attribute__((aligned(16))) T smem[2 * G::STAGE_ELEMS];
 
@@ -230,7 +272,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
         const int kv0 = j * BN;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int cidx = tid + kThreads * i;
+            const int cidx = tid + NT * i;
             const int row = cidx / (D / VEC);
             const int cc = cidx % (D / VEC);
             if (kv0 + row < Lk)
@@ -253,7 +295,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
         T* Vt = Ks + G::K_ELEMS;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int cidx = tid + kThreads * i;
+            const int cidx = tid + NT * i;
             const int row = cidx / (D / VEC);
             const int cc = cidx % (D / VEC);
             const int slot = (row & ~31) | k_slot(row & 31);
@@ -339,7 +381,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
                 for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[mb][nb][i]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = half_max(mx);
                 const float m_new = fmaxf(m_run[nb], mx * c);
                 // a row with no visible key yet keeps alpha = 1, P = 0
                 const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
@@ -358,8 +400,12 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
                 }
                 l_run[nb] = l_run[nb] * alpha + rs;
                 m_run[nb] = m_new;
+                // alpha == 1 exactly when the row max did not move; skip the
+                // multiply when that holds for every row of the wave
+                if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db][nb] *= alpha;
+                    for (int db = 0; db < NDB; ++db) oacc[db][nb] *= alpha;
+                }
             }
 
             // O^T += V^T P^T: rows = d, columns = queries
@@ -384,7 +430,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
     T* Oh = O + (size_t)bh * Lq * D;
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
-        const float lt = l_run[nb] + __shfl_xor(l_run[nb], 32);
+        const float lt = half_sum(l_run[nb]);
         const float inv = 1.0f / lt;
         const int row = q0w + nb * 32 + col;
         if (row < Lq) {
@@ -415,7 +461,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o,
     const long long nblocks = (long long)nqb * BH;
     const float c = scale * kLog2e;
     hipLaunchKernelGGL((fa_fwd_kernel<E, D, CAUSAL>), dim3((unsigned)nblocks),
-                       dim3(kThreads), 0, stream,
+                       dim3(G::NT), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), static_cast<T*>(o), lse,
                        BH, Lq, Lk, nqb, c);
@@ -446,7 +492,7 @@ hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
 
 template <class E, int D>
 TileConfig cfg_of() {
-    return TileConfig{Geom<E, D>::BM, Geom<E, D>::BN, kThreads};
+    return TileConfig{Geom<E, D>::BM, Geom<E, D>::BN, Geom<E, D>::NT};
 }
 
 }  // namespace

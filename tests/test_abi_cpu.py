@@ -58,7 +58,8 @@ def test_tile_config():
     for dt in ("bf16", "fp32"):
         for d in (64, 128, 256):
             bm, bn, th = fa.tile_config(dt, d)
-            assert bm % 32 == 0 and bn % 32 == 0 and th == 256
+            assert bm % 32 == 0 and bn % 32 == 0
+            assert th in (128, 256, 512) and bm % (th // 64 * 32) == 0
     with pytest.raises(fa.FAError):
         fa.tile_config("bf16", 96)
 
