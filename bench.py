@@ -112,6 +112,27 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None):
     }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "slices": done}
 
 
+def copy_calibration(mib: int, steps: int, warmup: int) -> int:
+    """Plain copy of a known byte count: reads and writes mib MiB per step."""
+    import torch
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read_per_step": n * 4,
+                      "copy_bytes_written_per_step": n * 4,
+                      "ms_per_step": dt * 1e3,
+                      "GB_per_s": 2 * n * 4 / dt / 1e9}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -126,6 +147,10 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="cap on (batch, head) slices in the CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device-to-device "
+                         "copy of MIB MiB per step (the known-size reference "
+                         "that HBM byte counters are scaled by)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -135,6 +160,8 @@ def main(argv=None):
         return 2
 
     import torch
+    if a.copy_calibration:
+        return copy_calibration(a.copy_calibration, a.steps, a.warmup)
     import exact_io_aware_08_amd as fa
     from seeded_inputs import WORKLOADS, workload_inputs
 

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["fa_fwd_kernel.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-fno-honor-nans"]
 
 
 def hipcc() -> str:
