@@ -224,3 +224,13 @@ def test_row_subset_and_workers_agree():
     Ow, Lw = attention_ref(q, k, v, True, 0.25, chunk=64, workers=4)
     np.testing.assert_array_equal(Ow, O)
     np.testing.assert_array_equal(Lw, L)
+
+
+def test_algorithmic_flops_closed_form():
+    from oracle import algorithmic_flops
+    L, d = 1000, 64
+    # causal: pairs (i, j) with j <= i -> L(L+1)/2; non-causal L*Lk
+    assert algorithmic_flops(np.arange(L), L, d, True) == 4 * d * L * (L + 1) / 2
+    assert algorithmic_flops(np.arange(L), 700, d, False) == 4 * d * L * 700
+    # causal with Lk < Lq: rows past Lk see all Lk keys
+    assert algorithmic_flops(np.arange(10), 4, 2, True) == 4 * 2 * (1 + 2 + 3 + 4 * 7)
