@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -449,6 +451,333 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
     }
 }
 
+// ===========================================================================
+// bf16 kernel with direct global->LDS tile loads (gfx950).
+//
+// K and V tiles are copied from HBM straight into LDS with
+// global_load_lds_dwordx4 (lane L of a wave instruction lands at byte 16*L
+// of a 1 KB LDS block), so no registers or VALU instructions stage them.
+// Both tiles keep their natural row layout [key][d] with the 16-byte chunks
+// of each row XOR-swizzled by the row index (conflict-free fragment reads);
+// each lane picks the global chunk that belongs at its LDS position.  The
+// V^T operand of the PV product is read with ds_read_b64_tr_b16: in each
+// 16-lane group, lane l receives element l%4 of the 8-byte rows supplied by
+// lanes (l%16)/4 + 4i (i = 0..3), so rows "4 keys x 4 d-quads" give every
+// lane 4 keys of its own d column; two such reads form one operand.
+// Tile rows at or beyond Lk are loaded from row Lk-1 (finite data that the
+// mask turns into weight 0).  The two tile buffers are separate LDS objects
+// and the key loop is unrolled by two, so each access names its buffer.
+// ===========================================================================
+
+#ifndef FA_DCFG_64
+#define FA_DCFG_64 128
+#endif
+#ifndef FA_DCFG_128
+#define FA_DCFG_128 128
+#endif
+#ifndef FA_DPRE
+#define FA_DPRE 4
+#endif
+#ifndef FA_DV0
+#define FA_DV0 48
+#endif
+#ifndef FA_DVN
+#define FA_DVN 6
+#endif
+template <int D> struct DCfg;
+template <> struct DCfg<64>  { static constexpr int BN = FA_DCFG_64; };
+template <> struct DCfg<128> { static constexpr int BN = FA_DCFG_128; };
+
+template <int D> struct DGeom {
+    static constexpr int NW = 8, NT = 512, WPE = 2;
+    static constexpr int BN = DCfg<D>::BN;
+    static constexpr int BM = NW * 32;             // 32 query rows per wave
+    static constexpr int NS = D / 16;              // MFMA steps along d for S
+    static constexpr int NMB = BN / 32;
+    static constexpr int NDB = D / 32;
+    static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    static constexpr int TILE = BN * D;            // elements per K or V tile
+    static constexpr int NBLK = BN * CPR / 64;     // 1 KB blocks per tile
+    static constexpr int BPW = NBLK / NW;          // blocks per wave per tile
+    static_assert(BPW * NW == NBLK && BPW >= 1, "tile / waves");
+    static_assert(BN % 32 == 0 && BM % BN == 0, "tile shape");
+    static_assert(4 * TILE * 2 <= 160 * 1024, "LDS budget");
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define FA_LDS __attribute__((address_space(3)))
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
+                          float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c)
+{
+    using G = DGeom<D>;
+    using E = BF16;
+    using Frag = bf16x8;
+    constexpr int BN = G::BN, BM = G::BM, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
+    constexpr int CPR = G::CPR, NW = G::NW;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t Kb0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Kb1[G::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vb0[G::TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vb1[G::TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+
+    int bh, lvl;
+    {
+        const int p = blockIdx.x;
+        if ((BH & 7) == 0) {
+            const int own = BH >> 3;
+            const int slot = p >> 3;
+            bh = (p & 7) + 8 * (slot % own);
+            lvl = slot / own;
+        } else {
+            bh = p % BH;
+            lvl = p / BH;
+        }
+    }
+    const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
+    const int q0 = qb * BM;
+    const int q0w = q0 + wave * 32;
+    const int qlast_w = q0w + 31;
+
+    const uint16_t* Qh = Q + (size_t)bh * Lq * D;
+    const uint16_t* Kh = K + (size_t)bh * Lk * D;
+    const uint16_t* Vh = V + (size_t)bh * Lk * D;
+
+    Frag qf[NS];
+    {
+        const int row = q0w + col;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            qf[s] = (row < Lq) ? E::load(Qh + (size_t)row * D + s * 16 + half * 8) : Frag{};
+    }
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+    float m_run = -__builtin_inff(), l_run = 0.f;
+
+    const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
+    const int nt = (kv_end + BN - 1) / BN;
+
+    // ---- tile copy: HBM -> LDS, no registers ------------------------------
+    // Per-lane parts of the copy addresses (element offsets inside a tile):
+    // LDS block blk of 64 chunks, lane's physical chunk p -> tile row and
+    // logical chunk.  K rows are stored in the permuted slot order of k_slot.
+    int kofs_g[G::BPW], vofs_g[G::BPW], krow_g[G::BPW], vrow_g[G::BPW];
+#pragma unroll
+    for (int i = 0; i < G::BPW; ++i) {
+        const int blk = wave + NW * i;
+        const int p = blk * 64 + lane;
+        const int row = p / CPR;
+        const int lc = (p % CPR) ^ (row & (CPR - 1));
+        const int kr = (row & ~31) | (16 * ((row >> 2) & 1) + 4 * ((row & 31) >> 3) + (row & 3));
+        krow_g[i] = kr;
+        vrow_g[i] = row;
+        kofs_g[i] = kr * D + lc * 8;
+        vofs_g[i] = row * D + lc * 8;
+    }
+    auto issue_loads = [&](int j, uint16_t* Kd, uint16_t* Vd) {
+        const int kv0 = j * BN;
+        const uint16_t* Kt = Kh + (size_t)kv0 * D;   // wave-uniform tile bases
+        const uint16_t* Vt = Vh + (size_t)kv0 * D;
+        const bool full = kv0 + BN <= Lk;
+#pragma unroll
+        for (int i = 0; i < G::BPW; ++i) {
+            const int blk = wave + NW * i;
+            int ko = kofs_g[i], vo = vofs_g[i];
+            if (!full) {   // rows at or past Lk read row Lk-1 instead
+                const int last = Lk - 1 - kv0;
+                ko += (min(krow_g[i], last) - krow_g[i]) * D;
+                vo += (min(vrow_g[i], last) - vrow_g[i]) * D;
+            }
+            __builtin_amdgcn_global_load_lds(Kt + ko, (FA_LDS void*)(Kd + blk * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Vt + vo, (FA_LDS void*)(Vd + blk * 512), 16, 0, 0);
+        }
+    };
+    // K fragment (A operand of S^T) for d-step s of key block mb: slot row
+    // mb*32 + col, logical chunk 2s + half, physical chunk XOR (row & CPR-1);
+    // mb only adds a whole-row offset, so one lane offset per s suffices.
+    int kfo[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) kfo[st] = col * D + (((2 * st + half) ^ (col & (CPR - 1))) * 8);
+    auto k_frag = [&](const uint16_t* Ks, int mb, int st) {
+        return E::load(Ks + mb * 32 * D + kfo[st]);
+    };
+    // V^T fragment for PV MFMA (mb, t, db): two transposed 8-byte reads.
+    // Lane l of 16-lane group g supplies row 16*(g>>1) + 8t + 4w + (l&15)/4
+    // of key block mb and d-quad 4*((l&15)%4) of the 16-column half g&1 of
+    // d-block db.  The XOR swizzle splits into a lane part (bits 0-1 of the
+    // chunk) and a compile-time part (bits >= 2), so one lane offset serves
+    // every (mb, t, db, w).
+    const int g16 = lane >> 4, rr = lane & 15;
+    const int vh = g16 >> 1, vdh = g16 & 1, vi = rr >> 2, vq = rr & 3;
+    const int vlane = (16 * vh + vi) * D + (((2 * vdh + (vq >> 1)) ^ vi) & 3) * 8 + (vq & 1) * 4;
+    auto v_frag = [&](const uint16_t* Vs, int mb, int t, int db) {
+        s16x4 u[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const int tw = ((8 * t + 4 * w) & (CPR - 1)) >> 2;   // compile-time swizzle bits
+            const int cofs = (mb * 32 + 8 * t + 4 * w) * D + ((db ^ tw) << 2) * 8;
+            const uint16_t* a = Vs + cofs + vlane;
+            u[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(FA_LDS void*)a);
+        }
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 v8 = __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(Frag, v8);
+    };
+
+    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
+        const int kv0 = j * BN;
+        if (j + 1 < nt) issue_loads(j + 1, Kn, Vn);
+        if (!CAUSAL || kv0 <= qlast_w) {
+            // S^T = K Q^T, K fragments read DPRE MFMAs ahead
+            f32x16 sacc[NMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) sacc[mb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+                    sacc[mb] = E::mfma(k_frag(Kc, mb, s), qf[s], sacc[mb]);
+#ifndef FA_NO_SCHED
+            {
+                constexpr int NM = NS * NMB, PRE = FA_DPRE;
+                __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+                for (int i = 0; i < NM - PRE; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+            }
+#endif
+            if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0w)) {
+                const int qi = q0w + col;
+#pragma unroll
+                for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kj = kv0 + mb * 32 + 16 * half + i;
+                        if ((kj >= Lk) || (CAUSAL && kj > qi)) sacc[mb][i] = -__builtin_inff();
+                    }
+            }
+            // row max: NMB independent 3-input chains, then combined
+            float pm[NMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                float a = fmaxf(fmaxf(sacc[mb][0], sacc[mb][1]), sacc[mb][2]);
+#pragma unroll
+                for (int i = 3; i < 15; i += 2) a = fmaxf(fmaxf(a, sacc[mb][i]), sacc[mb][i + 1]);
+                pm[mb] = fmaxf(a, sacc[mb][15]);
+            }
+#pragma unroll
+            for (int w = 1; w < NMB; w *= 2)
+#pragma unroll
+                for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
+            const float m_new = fmaxf(m_run, half_max(pm[0]) * c);
+            const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            // rescale O before the exponentials so that they and the PV
+            // MFMAs share one basic block (alpha == 1: skipped exactly)
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            }
+            m_run = m_new;
+            Frag pf[NMB][2];
+            float rsum[NMB];
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) {
+                float p[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -m_use));
+                const float s0 = (p[0] + p[1]) + (p[2] + p[3]);
+                const float s1 = (p[4] + p[5]) + (p[6] + p[7]);
+                const float s2 = (p[8] + p[9]) + (p[10] + p[11]);
+                const float s3 = (p[12] + p[13]) + (p[14] + p[15]);
+                rsum[mb] = (s0 + s1) + (s2 + s3);
+                pf[mb][0] = E::from_f32(p);
+                pf[mb][1] = E::from_f32(p + 8);
+            }
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        oacc[db] = E::mfma(v_frag(Vc, mb, t, db), pf[mb][t], oacc[db]);
+#ifndef FA_NO_SCHED
+            {
+                // exponentials of key block 0 first, then each PV MFMA with
+                // its two transposed reads and a share of the remaining VALU
+                constexpr int NM = NMB * 2 * NDB;
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0, 0);
+#pragma unroll
+                for (int i = 0; i < NM; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN, 0);
+                }
+            }
+#endif
+            float rs = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) rs += rsum[mb];
+            l_run = l_run * alpha + rs;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
+        __syncthreads();
+    };
+
+    issue_loads(0, Kb0, Vb0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int j = 0; j < nt; j += 2) {
+        step(j, Kb0, Vb0, Kb1, Vb1);
+        if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+    }
+
+    uint16_t* Oh = O + (size_t)bh * Lq * D;
+    const float lt = half_sum(l_run);
+    const float inv = 1.0f / lt;
+    const int row = q0w + col;
+    if (row < Lq) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 v4 = {oacc[db][4 * g + 0], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+                v4 *= inv;
+                E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
+            }
+        if (half == 0) LSE[(size_t)bh * Lq + row] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_direct(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Lq, int Lk, float scale, hipStream_t stream)
+{
+    using G = DGeom<D>;
+    const int BH = B * H;
+    const int nqb = (Lq + G::BM - 1) / G::BM;
+    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(G::NT),
+                       0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq, Lk,
+                       nqb, scale * kLog2e);
+    return hipGetLastError();
+}
+
 template <class E, int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o,
                       float* lse, int B, int H, int Lq, int Lk, float scale,
@@ -482,6 +811,16 @@ hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
                     float* lse, int B, int H, int Lq, int Lk, int d,
                     bool causal, float scale, hipStream_t stream)
 {
+#ifndef FA_NO_DIRECT
+    if constexpr (std::is_same<E, BF16>::value) {
+        if (d == 64)
+            return causal ? launch_direct<64, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
+                          : launch_direct<64, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
+        if (d == 128)
+            return causal ? launch_direct<128, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
+                          : launch_direct<128, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
+    }
+#endif
     switch (d) {
     case 64:  return launch_d<E, 64>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
     case 128: return launch_d<E, 128>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
@@ -501,8 +840,13 @@ bool tile_config(DType dt, int d, TileConfig* out)
 {
     if (dt == DType::BF16) {
         switch (d) {
+#ifndef FA_NO_DIRECT
+        case 64:  *out = TileConfig{DGeom<64>::BM, DGeom<64>::BN, DGeom<64>::NT}; return true;
+        case 128: *out = TileConfig{DGeom<128>::BM, DGeom<128>::BN, DGeom<128>::NT}; return true;
+#else
         case 64:  *out = cfg_of<BF16, 64>();  return true;
         case 128: *out = cfg_of<BF16, 128>(); return true;
+#endif
         case 256: *out = cfg_of<BF16, 256>(); return true;
         }
     } else if (dt == DType::F32) {
