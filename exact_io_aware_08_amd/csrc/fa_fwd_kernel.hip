@@ -469,11 +469,18 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // and the key loop is unrolled by two, so each access names its buffer.
 // ===========================================================================
 
+// keys per tile, waves per workgroup, waves per SIMD the registers are
+// sized for.  d = 64 runs 4 waves (128 query rows per workgroup): on short
+// causal sequences (B=4, H=16, L=1024) twice as many, smaller workgroups
+// balance the triangular grid better (21 us against 26 us with 8 waves).
 #ifndef FA_DCFG_64
-#define FA_DCFG_64 128
+#define FA_DCFG_64 128, 4, 2
 #endif
 #ifndef FA_DCFG_128
-#define FA_DCFG_128 128
+#define FA_DCFG_128 128, 8, 2
+#endif
+#ifndef FA_DCFG_256
+#define FA_DCFG_256 64, 4, 1
 #endif
 #ifndef FA_DPRE
 #define FA_DPRE 4
@@ -484,31 +491,40 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 #ifndef FA_DVN
 #define FA_DVN 6
 #endif
+template <int BN_, int NW_, int WPE_> struct DCfgT {
+    static constexpr int BN = BN_, NW = NW_, WPE = WPE_;
+};
 template <int D> struct DCfg;
-template <> struct DCfg<64>  { static constexpr int BN = FA_DCFG_64; };
-template <> struct DCfg<128> { static constexpr int BN = FA_DCFG_128; };
+template <> struct DCfg<64>  : DCfgT<FA_DCFG_64> {};
+template <> struct DCfg<128> : DCfgT<FA_DCFG_128> {};
+template <> struct DCfg<256> : DCfgT<FA_DCFG_256> {};
 
 template <int D> struct DGeom {
-    static constexpr int NW = 8, NT = 512, WPE = 2;
+    static constexpr int NW = DCfg<D>::NW, NT = 64 * NW, WPE = DCfg<D>::WPE;
     static constexpr int BN = DCfg<D>::BN;
     static constexpr int BM = NW * 32;             // 32 query rows per wave
     static constexpr int NS = D / 16;              // MFMA steps along d for S
     static constexpr int NMB = BN / 32;
     static constexpr int NDB = D / 32;
     static constexpr int CPR = D / 8;              // 16-byte chunks per row
+    // XOR swizzle mask on the chunk index: row & SWZ.  Capped at 16 chunks
+    // so that in a V^T read the swizzle bits of the row come only from
+    // (8t + 4w + lane), keeping lane and compile-time address parts apart.
+    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
     static constexpr int TILE = BN * D;            // elements per K or V tile
     static constexpr int NBLK = BN * CPR / 64;     // 1 KB blocks per tile
     static constexpr int BPW = NBLK / NW;          // blocks per wave per tile
     static_assert(BPW * NW == NBLK && BPW >= 1, "tile / waves");
     static_assert(BN % 32 == 0 && BM % BN == 0, "tile shape");
-    static_assert(4 * TILE * 2 <= 160 * 1024, "LDS budget");
+    static_assert(4 * TILE * 2 * (WPE * 4 / NW > 0 ? WPE * 4 / NW : 1) <= 160 * 1024, "LDS budget");
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__((DGeom<D>::NT))
+__attribute__((amdgpu_waves_per_eu(DGeom<D>::WPE, DGeom<D>::WPE)))
 void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c)
@@ -517,7 +533,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     using E = BF16;
     using Frag = bf16x8;
     constexpr int BN = G::BN, BM = G::BM, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
-    constexpr int CPR = G::CPR, NW = G::NW;
+    constexpr int CPR = G::CPR, NW = G::NW, SWZ = G::SWZ;
 
     __shared__ __attribute__((aligned(1024))) uint16_t Kb0[G::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Kb1[G::TILE];
@@ -577,7 +593,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int blk = wave + NW * i;
         const int p = blk * 64 + lane;
         const int row = p / CPR;
-        const int lc = (p % CPR) ^ (row & (CPR - 1));
+        const int lc = (p % CPR) ^ (row & SWZ);
         const int kr = (row & ~31) | (16 * ((row >> 2) & 1) + 4 * ((row & 31) >> 3) + (row & 3));
         krow_g[i] = kr;
         vrow_g[i] = row;
@@ -603,11 +619,11 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
     };
     // K fragment (A operand of S^T) for d-step s of key block mb: slot row
-    // mb*32 + col, logical chunk 2s + half, physical chunk XOR (row & CPR-1);
+    // mb*32 + col, logical chunk 2s + half, physical chunk XOR (row & SWZ);
     // mb only adds a whole-row offset, so one lane offset per s suffices.
     int kfo[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) kfo[st] = col * D + (((2 * st + half) ^ (col & (CPR - 1))) * 8);
+    for (int st = 0; st < NS; ++st) kfo[st] = col * D + (((2 * st + half) ^ (col & SWZ)) * 8);
     auto k_frag = [&](const uint16_t* Ks, int mb, int st) {
         return E::load(Ks + mb * 32 * D + kfo[st]);
     };
@@ -624,7 +640,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         s16x4 u[2];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            const int tw = ((8 * t + 4 * w) & (CPR - 1)) >> 2;   // compile-time swizzle bits
+            const int tw = ((8 * t + 4 * w) & SWZ) >> 2;   // compile-time swizzle bits
             const int cofs = (mb * 32 + 8 * t + 4 * w) * D + ((db ^ tw) << 2) * 8;
             const uint16_t* a = Vs + cofs + vlane;
             u[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(FA_LDS void*)a);
@@ -819,6 +835,9 @@ hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
         if (d == 128)
             return causal ? launch_direct<128, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
                           : launch_direct<128, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
+        if (d == 256)
+            return causal ? launch_direct<256, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
+                          : launch_direct<256, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
     }
 #endif
     switch (d) {
@@ -843,11 +862,12 @@ bool tile_config(DType dt, int d, TileConfig* out)
 #ifndef FA_NO_DIRECT
         case 64:  *out = TileConfig{DGeom<64>::BM, DGeom<64>::BN, DGeom<64>::NT}; return true;
         case 128: *out = TileConfig{DGeom<128>::BM, DGeom<128>::BN, DGeom<128>::NT}; return true;
+        case 256: *out = TileConfig{DGeom<256>::BM, DGeom<256>::BN, DGeom<256>::NT}; return true;
 #else
         case 64:  *out = cfg_of<BF16, 64>();  return true;
         case 128: *out = cfg_of<BF16, 128>(); return true;
-#endif
         case 256: *out = cfg_of<BF16, 256>(); return true;
+#endif
         }
     } else if (dt == DType::F32) {
         switch (d) {
