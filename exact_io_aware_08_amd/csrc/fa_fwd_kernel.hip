@@ -458,8 +458,10 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // global_load_lds_dwordx4 (lane L of a wave instruction lands at byte 16*L
 // of a 1 KB LDS block), so no registers or VALU instructions stage them.
 // Both tiles keep their natural row layout [key][d] with the 16-byte chunks
-// of each row XOR-swizzled by the row index (conflict-free fragment reads);
-// each lane picks the global chunk that belongs at its LDS position.  The
+// of each row XOR-swizzled by a function of the row index (a different one
+// for K and V, chosen so that both fragment reads are free of LDS bank
+// conflicts); each lane picks the global chunk that belongs at its LDS
+// position.  The
 // V^T operand of the PV product is read with ds_read_b64_tr_b16: in each
 // 16-lane group, lane l receives element l%4 of the 8-byte rows supplied by
 // lanes (l%16)/4 + 4i (i = 0..3), so rows "4 keys x 4 d-quads" give every
@@ -474,13 +476,13 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // causal sequences (B=4, H=16, L=1024) twice as many, smaller workgroups
 // balance the triangular grid better (21 us against 26 us with 8 waves).
 #ifndef FA_DCFG_64
-#define FA_DCFG_64 128, 4, 2
+#define FA_DCFG_64 128, 4, 2, 0
 #endif
 #ifndef FA_DCFG_128
-#define FA_DCFG_128 128, 8, 2
+#define FA_DCFG_128 128, 8, 2, 0
 #endif
 #ifndef FA_DCFG_256
-#define FA_DCFG_256 64, 4, 1
+#define FA_DCFG_256 64, 4, 1, 0
 #endif
 #ifndef FA_DPRE
 #define FA_DPRE 4
@@ -491,8 +493,9 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 #ifndef FA_DVN
 #define FA_DVN 6
 #endif
-template <int BN_, int NW_, int WPE_> struct DCfgT {
+template <int BN_, int NW_, int WPE_, int PP_> struct DCfgT {
     static constexpr int BN = BN_, NW = NW_, WPE = WPE_;
+    static constexpr bool PP = PP_ != 0;
 };
 template <int D> struct DCfg;
 template <> struct DCfg<64>  : DCfgT<FA_DCFG_64> {};
@@ -502,20 +505,35 @@ template <> struct DCfg<256> : DCfgT<FA_DCFG_256> {};
 template <int D> struct DGeom {
     static constexpr int NW = DCfg<D>::NW, NT = 64 * NW, WPE = DCfg<D>::WPE;
     static constexpr int BN = DCfg<D>::BN;
+    static constexpr bool PP = DCfg<D>::PP;        // two-phase wave groups
     static constexpr int BM = NW * 32;             // 32 query rows per wave
     static constexpr int NS = D / 16;              // MFMA steps along d for S
     static constexpr int NMB = BN / 32;
     static constexpr int NDB = D / 32;
     static constexpr int CPR = D / 8;              // 16-byte chunks per row
-    // XOR swizzle mask on the chunk index: row & SWZ.  Capped at 16 chunks
-    // so that in a V^T read the swizzle bits of the row come only from
-    // (8t + 4w + lane), keeping lane and compile-time address parts apart.
-    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+    // Chunk swizzles: logical chunk lc of tile row r sits at physical chunk
+    // lc ^ f(r).  LDS has 64 banks of 4 bytes, so the bank group (of 16)
+    // of a chunk is its position in the tile modulo 16.
+    //  * K is read with ds_read_b128, one slot row per lane: each pass of
+    //    16 lanes reads one logical chunk of 16 consecutive rows, so f_k
+    //    must give those rows 16 different bank groups.
+    //  * V is read with ds_read_b64_tr_b16: each 32-lane pass reads 4
+    //    logical chunks of 4 rows r0 + i (r0 a multiple of 4), so f_v must
+    //    give the 4 x 4 (row, chunk) pairs 16 different bank groups.  f_v
+    //    depends only on r & 3 (d >= 128) or bit 1 of r (d = 64), i.e. on
+    //    the lane, so the read addresses stay lane offset + constant.
+    __device__ static inline int f_k(int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static inline int f_v(int r) { return CPR >= 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
+    static constexpr int NVL = NDB < 4 ? NDB : 4;   // V^T lane offsets (one per db & 3)
     static constexpr int TILE = BN * D;            // elements per K or V tile
     static constexpr int NBLK = BN * CPR / 64;     // 1 KB blocks per tile
     static constexpr int BPW = NBLK / NW;          // blocks per wave per tile
     static_assert(BPW * NW == NBLK && BPW >= 1, "tile / waves");
     static_assert(BN % 32 == 0 && BM % BN == 0, "tile shape");
+    // waves w and w + 4 of a workgroup share a SIMD: the two groups of the
+    // staggered schedule need exactly two waves per SIMD
+    static_assert(!PP || (NW == 8 && WPE == 2), "staggered schedule geometry");
+    static_assert(BPW < 64, "vmcnt range");
     static_assert(4 * TILE * 2 * (WPE * 4 / NW > 0 ? WPE * 4 / NW : 1) <= 160 * 1024, "LDS budget");
 };
 
@@ -533,7 +551,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     using E = BF16;
     using Frag = bf16x8;
     constexpr int BN = G::BN, BM = G::BM, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
-    constexpr int CPR = G::CPR, NW = G::NW, SWZ = G::SWZ;
+    constexpr int CPR = G::CPR, NW = G::NW;
 
     __shared__ __attribute__((aligned(1024))) uint16_t Kb0[G::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Kb1[G::TILE];
@@ -593,56 +611,69 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int blk = wave + NW * i;
         const int p = blk * 64 + lane;
         const int row = p / CPR;
-        const int lc = (p % CPR) ^ (row & SWZ);
         const int kr = (row & ~31) | (16 * ((row >> 2) & 1) + 4 * ((row & 31) >> 3) + (row & 3));
         krow_g[i] = kr;
         vrow_g[i] = row;
-        kofs_g[i] = kr * D + lc * 8;
-        vofs_g[i] = row * D + lc * 8;
+        kofs_g[i] = kr * D + ((p % CPR) ^ G::f_k(row)) * 8;
+        vofs_g[i] = row * D + ((p % CPR) ^ G::f_v(row)) * 8;
     }
-    auto issue_loads = [&](int j, uint16_t* Kd, uint16_t* Vd) {
-        const int kv0 = j * BN;
-        const uint16_t* Kt = Kh + (size_t)kv0 * D;   // wave-uniform tile bases
-        const uint16_t* Vt = Vh + (size_t)kv0 * D;
-        const bool full = kv0 + BN <= Lk;
+    // Each wave copies BPW 1 KB blocks of a tile; rows at or past Lk read
+    // row Lk-1 instead (finite values that the mask gives weight 0).  The
+    // clamp is arithmetic and tile indexes past the last one are clamped to
+    // it, so every step issues the same copies without branches and the
+    // counted waits below stay exact.
+    auto issue_k = [&](int j, uint16_t* Kd) {
+        const int kv0 = min(j, nt - 1) * BN;
+        const uint16_t* Kt = Kh + (size_t)kv0 * D;   // wave-uniform tile base
+        const int last = Lk - 1 - kv0;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i) {
             const int blk = wave + NW * i;
-            int ko = kofs_g[i], vo = vofs_g[i];
-            if (!full) {   // rows at or past Lk read row Lk-1 instead
-                const int last = Lk - 1 - kv0;
-                ko += (min(krow_g[i], last) - krow_g[i]) * D;
-                vo += (min(vrow_g[i], last) - vrow_g[i]) * D;
-            }
+            const int ko = kofs_g[i] + (min(krow_g[i], last) - krow_g[i]) * D;
             __builtin_amdgcn_global_load_lds(Kt + ko, (FA_LDS void*)(Kd + blk * 512), 16, 0, 0);
+        }
+    };
+    auto issue_v = [&](int j, uint16_t* Vd) {
+        const int kv0 = min(j, nt - 1) * BN;
+        const uint16_t* Vt = Vh + (size_t)kv0 * D;
+        const int last = Lk - 1 - kv0;
+#pragma unroll
+        for (int i = 0; i < G::BPW; ++i) {
+            const int blk = wave + NW * i;
+            const int vo = vofs_g[i] + (min(vrow_g[i], last) - vrow_g[i]) * D;
             __builtin_amdgcn_global_load_lds(Vt + vo, (FA_LDS void*)(Vd + blk * 512), 16, 0, 0);
         }
     };
     // K fragment (A operand of S^T) for d-step s of key block mb: slot row
-    // mb*32 + col, logical chunk 2s + half, physical chunk XOR (row & SWZ);
-    // mb only adds a whole-row offset, so one lane offset per s suffices.
+    // mb*32 + col, logical chunk 2s + half; f_k(mb*32 + col) = f_k(col), so
+    // mb only adds a whole-row offset and one lane offset per s suffices.
     int kfo[NS];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) kfo[st] = col * D + (((2 * st + half) ^ (col & SWZ)) * 8);
+    for (int st = 0; st < NS; ++st) kfo[st] = col * D + (((2 * st + half) ^ G::f_k(col)) * 8);
     auto k_frag = [&](const uint16_t* Ks, int mb, int st) {
         return E::load(Ks + mb * 32 * D + kfo[st]);
     };
     // V^T fragment for PV MFMA (mb, t, db): two transposed 8-byte reads.
     // Lane l of 16-lane group g supplies row 16*(g>>1) + 8t + 4w + (l&15)/4
     // of key block mb and d-quad 4*((l&15)%4) of the 16-column half g&1 of
-    // d-block db.  The XOR swizzle splits into a lane part (bits 0-1 of the
-    // chunk) and a compile-time part (bits >= 2), so one lane offset serves
-    // every (mb, t, db, w).
+    // d-block db, i.e. logical chunk 4db + 2(g&1) + (l%4)/2.  The row's
+    // swizzle f_v depends only on the lane, and XORs bits 2.. of the chunk
+    // (the d-block bits) with a lane value, so the address is one of NVL
+    // lane offsets (chosen by db & 3) plus a compile-time constant.
     const int g16 = lane >> 4, rr = lane & 15;
     const int vh = g16 >> 1, vdh = g16 & 1, vi = rr >> 2, vq = rr & 3;
-    const int vlane = (16 * vh + vi) * D + (((2 * vdh + (vq >> 1)) ^ vi) & 3) * 8 + (vq & 1) * 4;
+    int vlane[G::NVL];
+#pragma unroll
+    for (int x = 0; x < G::NVL; ++x) {
+        const int lc = 4 * x + 2 * vdh + (vq >> 1);
+        vlane[x] = (16 * vh + vi) * D + (lc ^ G::f_v(vi)) * 8 + (vq & 1) * 4;
+    }
     auto v_frag = [&](const uint16_t* Vs, int mb, int t, int db) {
         s16x4 u[2];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
-            const int tw = ((8 * t + 4 * w) & SWZ) >> 2;   // compile-time swizzle bits
-            const int cofs = (mb * 32 + 8 * t + 4 * w) * D + ((db ^ tw) << 2) * 8;
-            const uint16_t* a = Vs + cofs + vlane;
+            const int cofs = (mb * 32 + 8 * t + 4 * w) * D + (db & ~3) * 32;
+            const uint16_t* a = Vs + cofs + vlane[db & (G::NVL - 1)];
             u[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(FA_LDS void*)a);
         }
         typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -650,119 +681,250 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         return __builtin_bit_cast(Frag, v8);
     };
 
-    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
-        const int kv0 = j * BN;
-        if (j + 1 < nt) issue_loads(j + 1, Kn, Vn);
-        if (!CAUSAL || kv0 <= qlast_w) {
-            // S^T = K Q^T, K fragments read DPRE MFMAs ahead
-            f32x16 sacc[NMB];
+    // ---- per-tile pieces ---------------------------------------------------
+    // S^T = K Q^T for the wave's 32 queries, K fragments read DPRE MFMAs ahead
+    auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NMB]) {
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) sacc[mb] = f32x16{};
+        for (int mb = 0; mb < NMB; ++mb) sacc[mb] = f32x16{};
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s)
 #pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-                    sacc[mb] = E::mfma(k_frag(Kc, mb, s), qf[s], sacc[mb]);
+            for (int mb = 0; mb < NMB; ++mb)
+                sacc[mb] = E::mfma(k_frag(Kc, mb, s), qf[s], sacc[mb]);
 #ifndef FA_NO_SCHED
-            {
-                constexpr int NM = NS * NMB, PRE = FA_DPRE;
-                __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+        constexpr int NM = NS * NMB, PRE = FA_DPRE;
+        __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
-                for (int i = 0; i < NM - PRE; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
-            }
+        for (int i = 0; i < NM - PRE; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
 #endif
-            if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0w)) {
-                const int qi = q0w + col;
-#pragma unroll
-                for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int kj = kv0 + mb * 32 + 16 * half + i;
-                        if ((kj >= Lk) || (CAUSAL && kj > qi)) sacc[mb][i] = -__builtin_inff();
-                    }
-            }
-            // row max: NMB independent 3-input chains, then combined
-            float pm[NMB];
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                float a = fmaxf(fmaxf(sacc[mb][0], sacc[mb][1]), sacc[mb][2]);
-#pragma unroll
-                for (int i = 3; i < 15; i += 2) a = fmaxf(fmaxf(a, sacc[mb][i]), sacc[mb][i + 1]);
-                pm[mb] = fmaxf(a, sacc[mb][15]);
-            }
-#pragma unroll
-            for (int w = 1; w < NMB; w *= 2)
-#pragma unroll
-                for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
-            const float m_new = fmaxf(m_run, half_max(pm[0]) * c);
-            const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            // rescale O before the exponentials so that they and the PV
-            // MFMAs share one basic block (alpha == 1: skipped exactly)
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-            }
-            m_run = m_new;
-            Frag pf[NMB][2];
-            float rsum[NMB];
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) {
-                float p[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -m_use));
-                const float s0 = (p[0] + p[1]) + (p[2] + p[3]);
-                const float s1 = (p[4] + p[5]) + (p[6] + p[7]);
-                const float s2 = (p[8] + p[9]) + (p[10] + p[11]);
-                const float s3 = (p[12] + p[13]) + (p[14] + p[15]);
-                rsum[mb] = (s0 + s1) + (s2 + s3);
-                pf[mb][0] = E::from_f32(p);
-                pf[mb][1] = E::from_f32(p + 8);
-            }
+    };
+    // mask, running max and O rescale; returns the max used by the
+    // exponentials and sets alpha
+    auto row_max = [&](int kv0, f32x16 (&sacc)[NMB], float& alpha) {
+        if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0w)) {
+            const int qi = q0w + col;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        oacc[db] = E::mfma(v_frag(Vc, mb, t, db), pf[mb][t], oacc[db]);
-#ifndef FA_NO_SCHED
-            {
-                // exponentials of key block 0 first, then each PV MFMA with
-                // its two transposed reads and a share of the remaining VALU
-                constexpr int NM = NMB * 2 * NDB;
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0, 0);
-#pragma unroll
-                for (int i = 0; i < NM; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN, 0);
+                for (int i = 0; i < 16; ++i) {
+                    const int kj = kv0 + mb * 32 + 16 * half + i;
+                    if ((kj >= Lk) || (CAUSAL && kj > qi)) sacc[mb][i] = -__builtin_inff();
                 }
-            }
-#endif
-            float rs = 0.f;
-#pragma unroll
-            for (int mb = 0; mb < NMB; ++mb) rs += rsum[mb];
-            l_run = l_run * alpha + rs;
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies landed
-        __syncthreads();
+        // NMB independent 3-input chains, then combined
+        float pm[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            float a = fmaxf(fmaxf(sacc[mb][0], sacc[mb][1]), sacc[mb][2]);
+#pragma unroll
+            for (int i = 3; i < 15; i += 2) a = fmaxf(fmaxf(a, sacc[mb][i]), sacc[mb][i + 1]);
+            pm[mb] = fmaxf(a, sacc[mb][15]);
+        }
+#pragma unroll
+        for (int w = 1; w < NMB; w *= 2)
+#pragma unroll
+            for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
+        const float m_new = fmaxf(m_run, half_max(pm[0]) * c);
+        const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        // rescale O before the exponentials so that they and the PV MFMAs
+        // can share one basic block (alpha == 1: skipped exactly)
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        m_run = m_new;
+        return m_use;
     };
+    // P = exp2(S c - m) as MFMA operands; returns this lane's partial sum
+    auto exps = [&](const f32x16 (&sacc)[NMB], float m_use, Frag (&pf)[NMB][2]) {
+        float rsum[NMB];
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mb][i], c, -m_use));
+            const float s0 = (p[0] + p[1]) + (p[2] + p[3]);
+            const float s1 = (p[4] + p[5]) + (p[6] + p[7]);
+            const float s2 = (p[8] + p[9]) + (p[10] + p[11]);
+            const float s3 = (p[12] + p[13]) + (p[14] + p[15]);
+            rsum[mb] = (s0 + s1) + (s2 + s3);
+            pf[mb][0] = E::from_f32(p);
+            pf[mb][1] = E::from_f32(p + 8);
+        }
+        float rs = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) rs += rsum[mb];
+        return rs;
+    };
+    // O^T += V^T P^T
+    auto pv = [&](const uint16_t* Vc, const Frag (&pf)[NMB][2]) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    oacc[db] = E::mfma(v_frag(Vc, mb, t, db), pf[mb][t], oacc[db]);
+    };
+    constexpr int NPVM = NMB * 2 * NDB;   // PV MFMAs per tile
+    // exponentials of key block 0 first, then each PV MFMA with its two
+    // transposed reads and a share of the remaining VALU work
+    auto sched_pv_valu = [&]() {
+#ifndef FA_NO_SCHED
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0, 0);
+#pragma unroll
+        for (int i = 0; i < NPVM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN, 0);
+        }
+#endif
+    };
+    // PV MFMAs alone, transposed reads DPRE MFMAs ahead
+    auto sched_pv_only = [&]() {
+#ifndef FA_NO_SCHED
+        constexpr int PRE = FA_DPRE;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PRE, 0);
+#pragma unroll
+        for (int i = 0; i < NPVM - PRE; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+#endif
+    };
+    // Wait until at most N of this wave's tile copies are in flight and its
+    // LDS reads are done, then the workgroup barrier.  A copy counts as done
+    // once its data is in LDS, so after the barrier every wave sees the
+    // tiles whose copies all waves waited for.  No memory fence: a
+    // workgroup-scope fence would wait for every copy in flight (vmcnt(0)),
+    // including the prefetch that is meant to overlap the next phase; the
+    // empty asm statements keep the compiler from moving memory accesses
+    // across the barrier.
+    auto sync_after = [&](auto n_in_flight) {
+        constexpr int N = decltype(n_in_flight)::value;
+        constexpr int imm = (N & 15) | ((N >> 4) << 14) | (7 << 4);   // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(imm);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    using InFlight0 = std::integral_constant<int, 0>;
+    using InFlightT = std::integral_constant<int, G::BPW>;
 
-    issue_loads(0, Kb0, Vb0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    for (int j = 0; j < nt; j += 2) {
-        step(j, Kb0, Vb0, Kb1, Vb1);
-        if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+    Frag pf[NMB][2];
+
+    if constexpr (!G::PP) {
+        // every wave: S_j, softmax_j, PV_j; copies of tile j+1 overlap
+        auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
+            const int kv0 = j * BN;
+            issue_k(j + 1, Kn);
+            issue_v(j + 1, Vn);
+            if (!CAUSAL || kv0 <= qlast_w) {
+                f32x16 sacc[NMB];
+                s_tile(Kc, sacc);
+                float alpha;
+                const float m_use = row_max(kv0, sacc, alpha);
+                const float rs = exps(sacc, m_use, pf);
+                pv(Vc, pf);
+                sched_pv_valu();
+                l_run = l_run * alpha + rs;
+            }
+            sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
+        };
+        issue_k(0, Kb0);
+        issue_v(0, Vb0);
+        sync_after(InFlight0{});
+        for (int j = 0; j < nt; j += 2) {
+            step(j, Kb0, Vb0, Kb1, Vb1);
+            if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+        }
+    } else {
+        // Two wave groups, staggered by half a tile so that on each SIMD one
+        // wave's softmax runs while the other wave's MFMAs do:
+        //   group A (waves 0..3):  S_j        | softmax_j + PV_j
+        //   group B (waves 4..7):  PV_{j-1}   | S_j + softmax_j
+        // with a workgroup barrier between the halves.  K_{j+1} is copied
+        // during the whole step; V_{j+1} is copied after the middle barrier,
+        // once group B has finished reading V_{j-1} from the same buffer.
+        // Each group runs its own copy of the loop, so neither carries the
+        // other's live registers across the barriers.  Both execute the same
+        // number of barriers: two per tile.
+        if (wave < NW / 2) {
+            auto step_a = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn,
+                              uint16_t* Vn) {
+                const int kv0 = j * BN;
+                const bool act = !CAUSAL || kv0 <= qlast_w;
+                issue_k(j + 1, Kn);
+                f32x16 sacc[NMB];
+                if (act) s_tile(Kc, sacc);
+                sync_after(InFlightT{});   // V_j landed; K_{j+1} may be in flight
+                issue_v(j + 1, Vn);
+                if (act) {
+                    float alpha;
+                    const float m_use = row_max(kv0, sacc, alpha);
+                    const float rs = exps(sacc, m_use, pf);
+                    pv(Vc, pf);
+                    sched_pv_valu();
+                    l_run = l_run * alpha + rs;
+                }
+                // K_{j+1} landed (V_{j+1} may still be in flight)
+                sync_after(InFlightT{});
+            };
+            issue_k(0, Kb0);
+            issue_v(0, Vb0);
+            sync_after(InFlight0{});
+            for (int j = 0; j < nt; j += 2) {
+                step_a(j, Kb0, Vb0, Kb1, Vb1);
+                if (j + 1 < nt) step_a(j + 1, Kb1, Vb1, Kb0, Vb0);
+            }
+        } else {
+            bool have_p = false;   // pf holds P^T of the previous tile
+            auto step_b = [&](int j, const uint16_t* Kc, const uint16_t* Vp, uint16_t* Kn,
+                              uint16_t* Vn) {
+                const int kv0 = j * BN;
+                const bool act = !CAUSAL || kv0 <= qlast_w;
+                issue_k(j + 1, Kn);
+                if (have_p) {
+                    pv(Vp, pf);
+                    sched_pv_only();
+                }
+                sync_after(InFlightT{});
+                issue_v(j + 1, Vn);   // into the buffer V_{j-1} used
+                if (act) {
+                    f32x16 sacc[NMB];
+                    s_tile(Kc, sacc);
+                    float alpha;
+                    const float m_use = row_max(kv0, sacc, alpha);
+                    const float rs = exps(sacc, m_use, pf);
+                    l_run = l_run * alpha + rs;
+                }
+                have_p = act;
+                sync_after(InFlightT{});
+            };
+            issue_k(0, Kb0);
+            issue_v(0, Vb0);
+            sync_after(InFlight0{});
+            for (int j = 0; j < nt; j += 2) {
+                step_b(j, Kb0, Vb1, Kb1, Vb1);
+                if (j + 1 < nt) step_b(j + 1, Kb1, Vb0, Kb0, Vb0);
+            }
+            // PV of the last tile (V_{nt-1} landed at the last middle barrier)
+            if (have_p) {
+                if ((nt - 1) & 1) pv(Vb1, pf);
+                else pv(Vb0, pf);
+            }
+        }
     }
 
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy left in flight
     uint16_t* Oh = O + (size_t)bh * Lq * D;
     const float lt = half_sum(l_run);
     const float inv = 1.0f / lt;

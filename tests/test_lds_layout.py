@@ -1,20 +1,29 @@
 """CPU model of the direct-load kernel's LDS layout (host-side index math).
 
 The bf16 kernel copies K and V tiles into LDS with global_load_lds (lane L
-of a wave instruction lands at 16-byte chunk L of a 1 KB block), XOR-swizzles
-the 16-byte chunks of every row, and reads the V^T operand with
-ds_read_b64_tr_b16, whose lane semantics (checked on the GPU with an
-in-bounds probe) are: in each 16-lane group, lane l receives element l % 4 of
-the 8-byte rows supplied by lanes (l % 16) // 4 + 4 i, i = 0..3.
+of a wave instruction lands at 16-byte chunk L of a 1 KB block), swizzles
+the 16-byte chunks of every row (logical chunk lc of row r sits at physical
+chunk lc ^ f(r), with one f for K and another for V), and reads the V^T
+operand with ds_read_b64_tr_b16, whose lane semantics (checked on the GPU
+with an in-bounds probe) are: in each 16-lane group, lane l receives element
+l % 4 of the 8-byte rows supplied by lanes (l % 16) // 4 + 4 i, i = 0..3.
 
-This test re-derives, for every lane, which (key, d) elements the K and V^T
-MFMA operands end up holding, and checks them against the operand layout the
+These tests re-derive, for every lane, which (key, d) elements the K and V^T
+MFMA operands end up holding, and check them against the operand layout the
 kernel assumes (v_mfma_f32_32x32x16_bf16: lane L holds row L % 32 and eight
 contraction elements for lane half L // 32; the P^T operand of lane half h,
-element e, of key block mb and step t is key mb*32 + 16h + 8t + e).  The
-formulas mirror the kernel's; a mismatch here means an addressing bug.
+element e, of key block mb and step t is key mb*32 + 16h + 8t + e).  They
+also count LDS bank cycles per read under a model of the LDS (64 banks of
+4 bytes; ds_read_b128 served 16 lanes per pass, 8-byte reads 32 lanes per
+pass; a pass costs the largest number of distinct words in one bank), which
+matched the bank-conflict counter of the previous layout.  The formulas
+mirror the kernel's; a mismatch here means an addressing bug.
 """
+import collections
+
 import pytest
+
+SHAPES = [(64, 128), (128, 128), (128, 64), (256, 64), (256, 32)]
 
 
 def k_slot_key(r):
@@ -22,43 +31,61 @@ def k_slot_key(r):
     return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3)
 
 
-def swz_mask(D):
-    cpr = D // 8
-    return min(cpr, 16) - 1
+def f_k(D, r):
+    return (r & 15) if D // 8 >= 16 else ((r >> 1) & 7)
 
 
-def lds_tile(D, BN, tensor):
-    """Physical element offset -> (key, d) after the DMA copies."""
+def f_v(D, r):
+    return ((r & 3) << 2) if D // 8 >= 16 else (((r >> 1) & 1) << 2)
+
+
+def lds_tile(D, BN, tensor, f):
+    """Physical element offset -> (key, d) after the copies."""
     cpr = D // 8
-    swz = swz_mask(D)
-    nblk = BN * cpr // 64
     cells = {}
-    for blk in range(nblk):
-        for lane in range(64):
-            p = blk * 64 + lane
-            row = p // cpr
-            lc = (p % cpr) ^ (row & swz)
-            if tensor == "K":
-                key = (row & ~31) | k_slot_key(row & 31)
-            else:
-                key = row
-            for e in range(8):
-                cells[p * 8 + e] = (key, lc * 8 + e)
+    for p in range(BN * cpr):   # block p // 64, lane p % 64
+        row = p // cpr
+        lc = (p % cpr) ^ f(D, row)
+        key = (row & ~31) | k_slot_key(row & 31) if tensor == "K" else row
+        for e in range(8):
+            cells[p * 8 + e] = (key, lc * 8 + e)
     assert len(cells) == BN * D
     return cells
 
 
-@pytest.mark.parametrize("D,BN", [(64, 128), (128, 128), (128, 64), (256, 64), (256, 32)])
+def k_addresses(D, mb, st, f=f_k):
+    """Element offsets of the K fragment reads (kernel: kfo[st] + mb*32*D)."""
+    out = []
+    for lane in range(64):
+        col, half = lane % 32, lane // 32
+        out.append(mb * 32 * D + col * D + (((2 * st + half) ^ f(D, col)) * 8))
+    return out
+
+
+def v_addresses(D, mb, t, db, w, f=f_v):
+    """Element offsets of one ds_read_b64_tr_b16 (kernel: cofs + vlane[db & 3])."""
+    nvl = min(D // 32, 4)
+    out = []
+    for lane in range(64):
+        g16, rr = lane >> 4, lane & 15
+        vh, vdh, vi, vq = g16 >> 1, g16 & 1, rr >> 2, rr & 3
+        x = db & (nvl - 1)
+        lc = 4 * x + 2 * vdh + (vq >> 1)
+        vlane = (16 * vh + vi) * D + (lc ^ f(D, vi)) * 8 + (vq & 1) * 4
+        cofs = (mb * 32 + 8 * t + 4 * w) * D + (db & ~3) * 32
+        out.append(cofs + vlane)
+    return out
+
+
+@pytest.mark.parametrize("D,BN", SHAPES)
 def test_k_operand_layout(D, BN):
-    cells = lds_tile(D, BN, "K")
-    swz = swz_mask(D)
+    cells = lds_tile(D, BN, "K", f_k)
     for mb in range(BN // 32):
         for st in range(D // 16):
+            addrs = k_addresses(D, mb, st)
             for lane in range(64):
                 col, half = lane % 32, lane // 32
-                kfo = col * D + (((2 * st + half) ^ (col & swz)) * 8)
-                a = mb * 32 * D + kfo
-                got = [cells[a + e] for e in range(8)]
+                got = [cells[addrs[lane] + e] for e in range(8)]
                 # S^T accumulator row r = col of key block mb holds key
                 # mb*32 + k_slot_key(col); contraction d = 16 st + 8 half + e
                 want = [(mb * 32 + k_slot_key(col), 16 * st + 8 * half + e)
@@ -76,26 +103,13 @@ def tr16(addresses, cells):
     return out
 
 
-@pytest.mark.parametrize("D,BN", [(64, 128), (128, 128), (128, 64), (256, 64), (256, 32)])
+@pytest.mark.parametrize("D,BN", SHAPES)
 def test_vt_operand_layout(D, BN):
-    cells = lds_tile(D, BN, "V")
-    swz = swz_mask(D)
+    cells = lds_tile(D, BN, "V", f_v)
     for mb in range(BN // 32):
         for t in range(2):
             for db in range(D // 32):
-                halves = []
-                for w in range(2):
-                    addrs = []
-                    for lane in range(64):
-                        g16, rr = lane >> 4, lane & 15
-                        vh, vdh, vi, vq = g16 >> 1, g16 & 1, rr >> 2, rr & 3
-                        vlane = ((16 * vh + vi) * D
-                                 + (((2 * vdh + (vq >> 1)) ^ vi) & 3) * 8
-                                 + (vq & 1) * 4)
-                        tw = ((8 * t + 4 * w) & swz) >> 2
-                        cofs = (mb * 32 + 8 * t + 4 * w) * D + ((db ^ tw) << 2) * 8
-                        addrs.append(cofs + vlane)
-                    halves.append(tr16(addrs, cells))
+                halves = [tr16(v_addresses(D, mb, t, db, w), cells) for w in range(2)]
                 for lane in range(64):
                     got = halves[0][lane] + halves[1][lane]
                     h = lane // 32
@@ -104,27 +118,33 @@ def test_vt_operand_layout(D, BN):
                     assert got == want, (D, BN, mb, t, db, lane, got[:3], want[:3])
 
 
-def test_old_mask_would_fail_for_d256():
-    """The unbounded swizzle mask (row & (D/8 - 1)) mixes the lane half into
-    the compile-time offset at d = 256; the model must detect that."""
-    D, BN = 256, 64
-    cpr = D // 8
-    cells = {}
-    for blk in range(BN * cpr // 64):
-        for lane in range(64):
-            p = blk * 64 + lane
-            row = p // cpr
-            lc = (p % cpr) ^ (row & (cpr - 1))
-            for e in range(8):
-                cells[p * 8 + e] = (row, lc * 8 + e)
-    bad = 0
-    for lane in range(64):
-        g16, rr = lane >> 4, lane & 15
-        vh, vdh, vi, vq = g16 >> 1, g16 & 1, rr >> 2, rr & 3
-        vlane = ((16 * vh + vi) * D + (((2 * vdh + (vq >> 1)) ^ vi) & 3) * 8
-                 + (vq & 1) * 4)
-        tw = ((8 * 0 + 4 * 0) & (cpr - 1)) >> 2
-        a = 0 * D + ((0 ^ tw) << 2) * 8 + vlane
-        if any(cells[a + c][1] // 32 != 0 for c in range(4)):
-            bad += 1
-    assert bad > 0
+def bank_cycles(elem_addrs, nbytes, pass_lanes):
+    tot = 0
+    for p in range(0, 64, pass_lanes):
+        banks = collections.defaultdict(set)
+        for a in elem_addrs[p:p + pass_lanes]:
+            for w in range(nbytes // 4):
+                word = a // 2 + w
+                banks[word % 64].add(word)
+        tot += max(len(s) for s in banks.values())
+    return tot
+
+
+@pytest.mark.parametrize("D,BN", SHAPES)
+def test_reads_are_bank_conflict_free(D, BN):
+    for mb in range(BN // 32):
+        for st in range(D // 16):
+            assert bank_cycles(k_addresses(D, mb, st), 16, 16) == 4
+        for t in range(2):
+            for db in range(D // 32):
+                for w in range(2):
+                    assert bank_cycles(v_addresses(D, mb, t, db, w), 8, 32) == 2
+
+
+def test_model_detects_conflicts_of_a_single_swizzle():
+    """The earlier layout (one XOR swizzle r & 15 for both tensors) puts the
+    4 rows of a transposed read on the same 16 banks; the model must see the
+    resulting 4-way conflict."""
+    same = lambda D, r: r & 15
+    assert bank_cycles(v_addresses(128, 0, 0, 0, 0, f=same), 8, 32) == 8
+    assert bank_cycles(k_addresses(64, 0, 0, f=lambda D, r: r & 7), 16, 16) == 8
