@@ -472,17 +472,18 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // ===========================================================================
 
 // keys per tile, waves per workgroup, waves per SIMD the registers are
-// sized for.  d = 64 runs 4 waves (128 query rows per workgroup): on short
+// sized for, 32-query blocks per wave (each K or V fragment read from LDS
+// feeds that many MFMAs).  d = 64 runs 4 waves (128 query rows per workgroup): on short
 // causal sequences (B=4, H=16, L=1024) twice as many, smaller workgroups
 // balance the triangular grid better (21 us against 26 us with 8 waves).
 #ifndef FA_DCFG_64
-#define FA_DCFG_64 128, 4, 2, 0
+#define FA_DCFG_64 128, 4, 2, 1
 #endif
 #ifndef FA_DCFG_128
-#define FA_DCFG_128 128, 8, 2, 0
+#define FA_DCFG_128 128, 8, 2, 1
 #endif
 #ifndef FA_DCFG_256
-#define FA_DCFG_256 64, 4, 1, 0
+#define FA_DCFG_256 64, 4, 1, 1
 #endif
 #ifndef FA_DPRE
 #define FA_DPRE 4
@@ -493,9 +494,8 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 #ifndef FA_DVN
 #define FA_DVN 6
 #endif
-template <int BN_, int NW_, int WPE_, int PP_> struct DCfgT {
-    static constexpr int BN = BN_, NW = NW_, WPE = WPE_;
-    static constexpr bool PP = PP_ != 0;
+template <int BN_, int NW_, int WPE_, int NBQ_> struct DCfgT {
+    static constexpr int BN = BN_, NW = NW_, WPE = WPE_, NBQ = NBQ_;
 };
 template <int D> struct DCfg;
 template <> struct DCfg<64>  : DCfgT<FA_DCFG_64> {};
@@ -505,8 +505,8 @@ template <> struct DCfg<256> : DCfgT<FA_DCFG_256> {};
 template <int D> struct DGeom {
     static constexpr int NW = DCfg<D>::NW, NT = 64 * NW, WPE = DCfg<D>::WPE;
     static constexpr int BN = DCfg<D>::BN;
-    static constexpr bool PP = DCfg<D>::PP;        // two-phase wave groups
-    static constexpr int BM = NW * 32;             // 32 query rows per wave
+    static constexpr int NBQ = DCfg<D>::NBQ;       // 32-query blocks per wave
+    static constexpr int BM = NW * 32 * NBQ;       // query rows per workgroup
     static constexpr int NS = D / 16;              // MFMA steps along d for S
     static constexpr int NMB = BN / 32;
     static constexpr int NDB = D / 32;
@@ -530,9 +530,6 @@ template <int D> struct DGeom {
     static constexpr int BPW = NBLK / NW;          // blocks per wave per tile
     static_assert(BPW * NW == NBLK && BPW >= 1, "tile / waves");
     static_assert(BN % 32 == 0 && BM % BN == 0, "tile shape");
-    // waves w and w + 4 of a workgroup share a SIMD: the two groups of the
-    // staggered schedule need exactly two waves per SIMD
-    static_assert(!PP || (NW == 8 && WPE == 2), "staggered schedule geometry");
     static_assert(BPW < 64, "vmcnt range");
     static_assert(4 * TILE * 2 * (WPE * 4 / NW > 0 ? WPE * 4 / NW : 1) <= 160 * 1024, "LDS budget");
 };
@@ -551,7 +548,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     using E = BF16;
     using Frag = bf16x8;
     constexpr int BN = G::BN, BM = G::BM, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
-    constexpr int CPR = G::CPR, NW = G::NW;
+    constexpr int CPR = G::CPR, NW = G::NW, NBQ = G::NBQ;
 
     __shared__ __attribute__((aligned(1024))) uint16_t Kb0[G::TILE];
     __shared__ __attribute__((aligned(1024))) uint16_t Kb1[G::TILE];
@@ -579,24 +576,30 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     }
     const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
     const int q0 = qb * BM;
-    const int q0w = q0 + wave * 32;
-    const int qlast_w = q0w + 31;
+    const int q0w = q0 + wave * 32 * NBQ;   // query block nb: rows q0w + 32 nb + col
+    const int qlast_w = q0w + 32 * NBQ - 1;
 
     const uint16_t* Qh = Q + (size_t)bh * Lq * D;
     const uint16_t* Kh = K + (size_t)bh * Lk * D;
     const uint16_t* Vh = V + (size_t)bh * Lk * D;
 
-    Frag qf[NS];
-    {
-        const int row = q0w + col;
+    Frag qf[NBQ][NS];
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const int row = q0w + 32 * nb + col;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            qf[s] = (row < Lq) ? E::load(Qh + (size_t)row * D + s * 16 + half * 8) : Frag{};
+            qf[nb][s] = (row < Lq) ? E::load(Qh + (size_t)row * D + s * 16 + half * 8) : Frag{};
     }
-    f32x16 oacc[NDB];
+    f32x16 oacc[NBQ][NDB];
+    float m_run[NBQ], l_run[NBQ];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-    float m_run = -__builtin_inff(), l_run = 0.f;
+    for (int nb = 0; nb < NBQ; ++nb) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[nb][db] = f32x16{};
+        m_run[nb] = -__builtin_inff();
+        l_run[nb] = 0.f;
+    }
 
     const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
     const int nt = (kv_end + BN - 1) / BN;
@@ -682,31 +685,38 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
 
     // ---- per-tile pieces ---------------------------------------------------
-    // S^T = K Q^T for the wave's 32 queries, K fragments read DPRE MFMAs ahead
-    auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NMB]) {
+    // S^T = K Q^T for the wave's NBQ query blocks; each K fragment feeds NBQ
+    // MFMAs and is read DPRE fragments ahead
+    auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NBQ][NMB]) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) sacc[mb] = f32x16{};
+        for (int nb = 0; nb < NBQ; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb) sacc[nb][mb] = f32x16{};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
-                sacc[mb] = E::mfma(k_frag(Kc, mb, s), qf[s], sacc[mb]);
+            for (int mb = 0; mb < NMB; ++mb) {
+                const Frag a = k_frag(Kc, mb, s);
+#pragma unroll
+                for (int nb = 0; nb < NBQ; ++nb) sacc[nb][mb] = E::mfma(a, qf[nb][s], sacc[nb][mb]);
+            }
 #ifndef FA_NO_SCHED
-        constexpr int NM = NS * NMB, PRE = FA_DPRE;
+        constexpr int NK = NS * NMB, PRE = FA_DPRE;
         __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
-        for (int i = 0; i < NM - PRE; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < NK - PRE; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NBQ, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PRE * NBQ, 0);
 #endif
     };
-    // mask, running max and O rescale; returns the max used by the
-    // exponentials and sets alpha
-    auto row_max = [&](int kv0, f32x16 (&sacc)[NMB], float& alpha) {
-        if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0w)) {
-            const int qi = q0w + col;
+    // mask, running max and O rescale for query block nb; returns the max
+    // used by the exponentials and sets alpha
+    auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha) {
+        const int qb0 = q0w + 32 * nb;
+        if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > qb0)) {
+            const int qi = qb0 + col;
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -728,16 +738,16 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         for (int w = 1; w < NMB; w *= 2)
 #pragma unroll
             for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
-        const float m_new = fmaxf(m_run, half_max(pm[0]) * c);
+        const float m_new = fmaxf(m_run[nb], half_max(pm[0]) * c);
         const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         // rescale O before the exponentials so that they and the PV MFMAs
         // can share one basic block (alpha == 1: skipped exactly)
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < NDB; ++db) oacc[nb][db] *= alpha;
         }
-        m_run = m_new;
+        m_run[nb] = m_new;
         return m_use;
     };
     // P = exp2(S c - m) as MFMA operands; returns this lane's partial sum
@@ -762,42 +772,33 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         for (int mb = 0; mb < NMB; ++mb) rs += rsum[mb];
         return rs;
     };
-    // O^T += V^T P^T
-    auto pv = [&](const uint16_t* Vc, const Frag (&pf)[NMB][2]) {
+    // O^T += V^T P^T; each V^T fragment feeds NBQ MFMAs
+    auto pv = [&](const uint16_t* Vc, const Frag (&pf)[NBQ][NMB][2]) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    oacc[db] = E::mfma(v_frag(Vc, mb, t, db), pf[mb][t], oacc[db]);
+                for (int db = 0; db < NDB; ++db) {
+                    const Frag v = v_frag(Vc, mb, t, db);
+#pragma unroll
+                    for (int nb = 0; nb < NBQ; ++nb)
+                        oacc[nb][db] = E::mfma(v, pf[nb][mb][t], oacc[nb][db]);
+                }
     };
-    constexpr int NPVM = NMB * 2 * NDB;   // PV MFMAs per tile
-    // exponentials of key block 0 first, then each PV MFMA with its two
-    // transposed reads and a share of the remaining VALU work
+    // exponentials of key block 0 first, then each V^T fragment's MFMAs
+    // with its two transposed reads and a share of the remaining VALU work
     auto sched_pv_valu = [&]() {
 #ifndef FA_NO_SCHED
+        constexpr int NV = NMB * 2 * NDB;   // V^T fragments per tile
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0 * NBQ, 0);
 #pragma unroll
-        for (int i = 0; i < NPVM; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < NV; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NBQ, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN * NBQ, 0);
         }
-#endif
-    };
-    // PV MFMAs alone, transposed reads DPRE MFMAs ahead
-    auto sched_pv_only = [&]() {
-#ifndef FA_NO_SCHED
-        constexpr int PRE = FA_DPRE;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PRE, 0);
-#pragma unroll
-        for (int i = 0; i < NPVM - PRE; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
 #endif
     };
     // Wait until at most N of this wave's tile copies are in flight and its
@@ -817,128 +818,57 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         asm volatile("" ::: "memory");
     };
     using InFlight0 = std::integral_constant<int, 0>;
-    using InFlightT = std::integral_constant<int, G::BPW>;
 
-    Frag pf[NMB][2];
-
-    if constexpr (!G::PP) {
-        // every wave: S_j, softmax_j, PV_j; copies of tile j+1 overlap
-        auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
-            const int kv0 = j * BN;
-            issue_k(j + 1, Kn);
-            issue_v(j + 1, Vn);
-            if (!CAUSAL || kv0 <= qlast_w) {
-                f32x16 sacc[NMB];
-                s_tile(Kc, sacc);
-                float alpha;
-                const float m_use = row_max(kv0, sacc, alpha);
-                const float rs = exps(sacc, m_use, pf);
-                pv(Vc, pf);
-                sched_pv_valu();
-                l_run = l_run * alpha + rs;
+    // every wave: S_j, softmax_j, PV_j; the copies of tile j+1 overlap them
+    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
+        const int kv0 = j * BN;
+        issue_k(j + 1, Kn);
+        issue_v(j + 1, Vn);
+        if (!CAUSAL || kv0 <= qlast_w) {
+            f32x16 sacc[NBQ][NMB];
+            s_tile(Kc, sacc);
+            float alpha[NBQ], rs[NBQ];
+            Frag pf[NBQ][NMB][2];
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                const float m_use = row_max(kv0, nb, sacc[nb], alpha[nb]);
+                rs[nb] = exps(sacc[nb], m_use, pf[nb]);
             }
-            sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
-        };
-        issue_k(0, Kb0);
-        issue_v(0, Vb0);
-        sync_after(InFlight0{});
-        for (int j = 0; j < nt; j += 2) {
-            step(j, Kb0, Vb0, Kb1, Vb1);
-            if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+            pv(Vc, pf);
+            sched_pv_valu();
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
         }
-    } else {
-        // Two wave groups, staggered by half a tile so that on each SIMD one
-        // wave's softmax runs while the other wave's MFMAs do:
-        //   group A (waves 0..3):  S_j        | softmax_j + PV_j
-        //   group B (waves 4..7):  PV_{j-1}   | S_j + softmax_j
-        // with a workgroup barrier between the halves.  K_{j+1} is copied
-        // during the whole step; V_{j+1} is copied after the middle barrier,
-        // once group B has finished reading V_{j-1} from the same buffer.
-        // Each group runs its own copy of the loop, so neither carries the
-        // other's live registers across the barriers.  Both execute the same
-        // number of barriers: two per tile.
-        if (wave < NW / 2) {
-            auto step_a = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn,
-                              uint16_t* Vn) {
-                const int kv0 = j * BN;
-                const bool act = !CAUSAL || kv0 <= qlast_w;
-                issue_k(j + 1, Kn);
-                f32x16 sacc[NMB];
-                if (act) s_tile(Kc, sacc);
-                sync_after(InFlightT{});   // V_j landed; K_{j+1} may be in flight
-                issue_v(j + 1, Vn);
-                if (act) {
-                    float alpha;
-                    const float m_use = row_max(kv0, sacc, alpha);
-                    const float rs = exps(sacc, m_use, pf);
-                    pv(Vc, pf);
-                    sched_pv_valu();
-                    l_run = l_run * alpha + rs;
-                }
-                // K_{j+1} landed (V_{j+1} may still be in flight)
-                sync_after(InFlightT{});
-            };
-            issue_k(0, Kb0);
-            issue_v(0, Vb0);
-            sync_after(InFlight0{});
-            for (int j = 0; j < nt; j += 2) {
-                step_a(j, Kb0, Vb0, Kb1, Vb1);
-                if (j + 1 < nt) step_a(j + 1, Kb1, Vb1, Kb0, Vb0);
-            }
-        } else {
-            bool have_p = false;   // pf holds P^T of the previous tile
-            auto step_b = [&](int j, const uint16_t* Kc, const uint16_t* Vp, uint16_t* Kn,
-                              uint16_t* Vn) {
-                const int kv0 = j * BN;
-                const bool act = !CAUSAL || kv0 <= qlast_w;
-                issue_k(j + 1, Kn);
-                if (have_p) {
-                    pv(Vp, pf);
-                    sched_pv_only();
-                }
-                sync_after(InFlightT{});
-                issue_v(j + 1, Vn);   // into the buffer V_{j-1} used
-                if (act) {
-                    f32x16 sacc[NMB];
-                    s_tile(Kc, sacc);
-                    float alpha;
-                    const float m_use = row_max(kv0, sacc, alpha);
-                    const float rs = exps(sacc, m_use, pf);
-                    l_run = l_run * alpha + rs;
-                }
-                have_p = act;
-                sync_after(InFlightT{});
-            };
-            issue_k(0, Kb0);
-            issue_v(0, Vb0);
-            sync_after(InFlight0{});
-            for (int j = 0; j < nt; j += 2) {
-                step_b(j, Kb0, Vb1, Kb1, Vb1);
-                if (j + 1 < nt) step_b(j + 1, Kb1, Vb0, Kb0, Vb0);
-            }
-            // PV of the last tile (V_{nt-1} landed at the last middle barrier)
-            if (have_p) {
-                if ((nt - 1) & 1) pv(Vb1, pf);
-                else pv(Vb0, pf);
-            }
-        }
+        sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
+    };
+    issue_k(0, Kb0);
+    issue_v(0, Vb0);
+    sync_after(InFlight0{});
+    for (int j = 0; j < nt; j += 2) {
+        step(j, Kb0, Vb0, Kb1, Vb1);
+        if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
     }
 
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy left in flight
     uint16_t* Oh = O + (size_t)bh * Lq * D;
-    const float lt = half_sum(l_run);
-    const float inv = 1.0f / lt;
-    const int row = q0w + col;
-    if (row < Lq) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+    for (int nb = 0; nb < NBQ; ++nb) {
+        const float lt = half_sum(l_run[nb]);
+        const float inv = 1.0f / lt;
+        const int row = q0w + 32 * nb + col;
+        if (row < Lq) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                f32x4 v4 = {oacc[db][4 * g + 0], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-                v4 *= inv;
-                E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
-            }
-        if (half == 0) LSE[(size_t)bh * Lq + row] = (m_run + __builtin_amdgcn_logf(lt)) * kLn2;
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v4 = {oacc[nb][db][4 * g + 0], oacc[nb][db][4 * g + 1],
+                                oacc[nb][db][4 * g + 2], oacc[nb][db][4 * g + 3]};
+                    v4 *= inv;
+                    E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
+                }
+            if (half == 0)
+                LSE[(size_t)bh * Lq + row] = (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2;
+        }
     }
 }
 
