@@ -41,8 +41,14 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source with comments and whitespace removed, so
+    that counters stay attached to the code they were taken on and survive
+    edits that cannot change it."""
+    text = open(KERNEL_SOURCE).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def traffic_from_profiles(workload: str):

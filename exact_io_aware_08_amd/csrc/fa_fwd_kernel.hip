@@ -19,6 +19,12 @@
 //  * causal: tiles right of the diagonal are never visited, tiles that
 //    straddle it are masked element-wise (same page, section 4).
 //
+// Two kernels share that method.  fa_fwd_direct_kernel serves bf16: K and V
+// tiles go from HBM straight into LDS (global_load_lds, no registers), and
+// the V^T operand is read with the transposing ds_read_b64_tr_b16.
+// fa_fwd_kernel serves fp32: tiles are staged through registers and V is
+// written to LDS transposed.
+//
 // gfx950 mapping (not the pages' Triton tiling):
 //  * each wave owns 32*NBQ query rows; the NW waves of a workgroup share
 //    one K/V tile in LDS;
@@ -30,10 +36,9 @@
 //    already the P^T operand of the next MFMA (no LDS round trip for P);
 //  * K rows are stored in LDS in a permuted order so that lane half h's
 //    accumulator rows are the 16 consecutive keys 16h..16h+15 of each
-//    32-key block; V is stored transposed (V^T, keys contiguous) so each
-//    P^T V^T operand is one 16-byte LDS read;
-//  * K/V tiles are double-buffered: tile j+1 is fetched from HBM into
-//    registers while tile j is computed, then written to the other buffer;
+//    32-key block, so every P^T operand is 8 consecutive keys;
+//  * K/V tiles are double-buffered: the copy of tile j+1 runs while tile j
+//    is computed;
 //  * workgroup ids are remapped so that all query blocks of a head run on
 //    one XCD (its L2 serves the K/V re-reads) and, for causal, the
 //    heaviest query blocks start first.
@@ -561,6 +566,10 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int col = lane & 31;
     const int half = lane >> 5;
 
+    // ---- work decode: XCD-grouped heads, heaviest causal blocks first ----
+    // Workgroups are dispatched round-robin over the 8 XCDs, so block id p
+    // runs on XCD p % 8; every query block of a head goes to one XCD (its L2
+    // serves the K/V re-reads) and, causal, the longest rows start first.
     int bh, lvl;
     {
         const int p = blockIdx.x;
@@ -583,6 +592,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const uint16_t* Kh = K + (size_t)bh * Lk * D;
     const uint16_t* Vh = V + (size_t)bh * Lk * D;
 
+    // ---- Q fragments: resident for the whole key loop --------------------
     Frag qf[NBQ][NS];
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
@@ -849,6 +859,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
     }
 
+    // ---- epilogue: O / l, LSE = ln2 * (m + log2 l) -------------------------
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy left in flight
     uint16_t* Oh = O + (size_t)bh * Lq * D;
 #pragma unroll
