@@ -16,7 +16,9 @@ IO æ„ŸçŸ¥èƒ½åŠ›"; the log-sum-exp output, "ç¬¬ 08 ç« : Flash Attentionâ€”â€”åˆ†å
 "å› æœæ©ç çš„åˆ†å—éå†", lower triangle including the diagonal):
 
   1. s_ij  = scale * sum_d q_id k_jd                 (fp64, j < Lk)
-  2. A_i   = {j < Lk}  (non-causal)  or  {j < Lk : j <= i}  (causal)
+  2. A_i   = {j < Lk}  (non-causal)  or  {j < Lk : j <= i}  (causal),
+     intersected, for a sliding window (left, right), with
+     {j : i - left <= j <= i + right} (either bound may be absent)
   3. m_i   = max_{j in A_i} s_ij ;  l_i = sum_{j in A_i} exp(s_ij - m_i)
   4. P_ij  = exp(s_ij - m_i) / l_i  for j in A_i, else 0
   5. O_i   = sum_j P_ij v_j
@@ -26,11 +28,18 @@ Subtracting m_i in step 3 is the safe-softmax form of the same quantity
 ("FlashAttentionçš„Tritonå®ç°ï¼šIO-awareæ³¨æ„åŠ›æœºåˆ¶åº•å±‚åŸç†", gitcode.csdn.net,
 section "Safe Softmax çš„æ•°å­¦æ¨å¯¼"); it changes nothing mathematically.
 
+The sliding window follows the pages' window-size pair (left, right) used
+together with the causal flag ("Flash Attention åŸç†ä¸å®ç°è¯¦è§£" (tbr8.org),
+section 6.3 "æ»‘åŠ¨çª—å£æ³¨æ„åŠ›", where (1024, 0) means 1024 keys to the left and
+none to the right).
+
 Readings where the pages are silent or disagree (each listed in the design
 notes): LSE uses the natural log of the scaled scores; causal alignment is
 top-left (key j visible to query i iff j <= i) for any Lq, Lk; masked keys
 are excluded exactly (weight 0), not given a large negative score; keys at
-or beyond Lk never take part.
+or beyond Lk never take part; a window bound w admits keys at distance up to
+and including w; a row left with no key (possible only with a left bound
+and Lq > Lk) has O = 0 and LSE = -inf.
 
 S and P are formed explicitly, one (b, h, row-chunk) at a time to bound
 memory.  A thread pool over those chunks keeps BLAS at one thread per worker.
@@ -49,33 +58,45 @@ except Exception:  # pragma: no cover
     threadpool_limits = None
 
 
-def _chunk_ref(q64, k64, v64, rows, causal, scale, want_p):
+def _chunk_ref(q64, k64, v64, rows, causal, scale, want_p, window=None):
     """One (b, h, row-chunk): q64 [R, d] rows at absolute indices ``rows``."""
-    # columns that any row of this chunk may see
+    left, right = window if window is not None else (None, None)
     Lk = k64.shape[0]
-    ncols = Lk if not causal else min(Lk, int(rows.max()) + 1)
-    s = (q64 @ k64[:ncols].T) * scale                        # step 1
-    if causal:                                               # step 2
-        allowed = np.arange(ncols)[None, :] <= rows[:, None]
-    else:
-        allowed = np.ones((len(rows), ncols), dtype=bool)
+    # columns that any row of this chunk may see
+    hi = Lk
+    if causal:
+        hi = min(hi, int(rows.max()) + 1)
+    if right is not None:
+        hi = min(hi, int(rows.max()) + right + 1)
+    lo = 0 if left is None else max(0, int(rows.min()) - left)
+    hi = max(hi, lo)
+    cols = np.arange(lo, hi)
+    s = (q64 @ k64[lo:hi].T) * scale                         # step 1
+    allowed = np.ones((len(rows), len(cols)), dtype=bool)    # step 2
+    if causal:
+        allowed &= cols[None, :] <= rows[:, None]
+    if left is not None:
+        allowed &= cols[None, :] >= rows[:, None] - left
+    if right is not None:
+        allowed &= cols[None, :] <= rows[:, None] + right
     s_masked = np.where(allowed, s, -np.inf)
-    m = s_masked.max(axis=1)                                 # step 3
-    e = np.where(allowed, np.exp(s_masked - m[:, None]), 0.0)
-    l = e.sum(axis=1)
-    p = e / l[:, None]                                       # step 4
-    o = p @ v64[:ncols]                                      # step 5
-    lse = m + np.log(l)                                      # step 6
+    with np.errstate(invalid="ignore", divide="ignore"):
+        m = s_masked.max(axis=1, initial=-np.inf)            # step 3
+        e = np.where(allowed, np.exp(s_masked - m[:, None]), 0.0)
+        l = e.sum(axis=1)
+        p = e / np.where(l > 0, l, 1.0)[:, None]             # step 4 (empty row: 0)
+        o = p @ v64[lo:hi]                                   # step 5
+        lse = m + np.log(l)                                  # step 6 (empty row: -inf)
     if want_p:
         full = np.zeros((len(rows), Lk))
-        full[:, :ncols] = p
+        full[:, lo:hi] = p
         return o, lse, full
     return o, lse, None
 
 
 def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
                   return_p: bool = False, workers: int | None = None,
-                  chunk: int = 512):
+                  chunk: int = 512, window=None):
     """fp64 attention forward.
 
     q: [B, H, Lq, d]; k, v: [B, H, Lk, d]; any real dtype (widened exactly
@@ -83,6 +104,9 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
     same fp32 value the GPU receives).  ``rows``: optional 1-D array of
     query indices to evaluate (each output row depends only on its own q row
     and on all of K, V, so a subset is the same definition).
+
+    ``window``: optional (left, right) sliding window; each entry a
+    non-negative int or None (no bound on that side).
 
     Returns O [B, H, R, d] and LSE [B, H, R] in fp64 (R = Lq or len(rows)),
     plus P [B, H, R, Lk] when ``return_p``.
@@ -99,6 +123,8 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
         rows = np.arange(Lq)
     rows = np.asarray(rows, dtype=np.int64)
     assert rows.ndim == 1 and (rows >= 0).all() and (rows < Lq).all()
+    if window is not None:
+        assert len(window) == 2 and all(w is None or int(w) >= 0 for w in window)
     R = len(rows)
     O = np.empty((B, H, R, d))
     LSE = np.empty((B, H, R))
@@ -114,7 +140,7 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
         b, h, c0, c1 = job
         r = rows[c0:c1]
         o, lse, p = _chunk_ref(q[b, h, r], k[b, h], v[b, h], r, causal,
-                               scale, return_p)
+                               scale, return_p, window)
         O[b, h, c0:c1] = o
         LSE[b, h, c0:c1] = lse
         if return_p:
@@ -148,16 +174,22 @@ def default_workers() -> int:
         return os.cpu_count() or 1
 
 
-def algorithmic_flops(Lq_rows, Lk: int, d: int, causal: bool) -> float:
+def algorithmic_flops(Lq_rows, Lk: int, d: int, causal: bool, window=None) -> float:
     """Matmul flops of the method for the given query rows of one head:
     4*d per visible (query, key) pair, the count used for TFLOP/s
     ("ç¬¬ 08 ç« " benchmark harness: 2 matmuls x 2 flops per MAC, halved for
     the causal mask at full size)."""
     rows = np.asarray(Lq_rows, dtype=np.int64)
+    left, right = window if window is not None else (None, None)
+    hi = np.full(rows.shape, Lk - 1)
     if causal:
-        vis = np.minimum(rows + 1, Lk)
-    else:
-        vis = np.full(rows.shape, Lk)
+        hi = np.minimum(hi, rows)
+    if right is not None:
+        hi = np.minimum(hi, rows + right)
+    lo = np.zeros(rows.shape, dtype=np.int64)
+    if left is not None:
+        lo = np.maximum(lo, rows - left)
+    vis = np.maximum(hi - lo + 1, 0)
     return float(4.0 * d * vis.sum())
 
 

@@ -31,14 +31,31 @@ def rng_qkv(seed, B, H, Lq, Lk, d, sigma=1.0):
     return q, k, v
 
 
-def brute_force(q, k, v, causal, scale):
-    """q [Lq,d], k,v [Lk,d] -> O [Lq,d], LSE [Lq] with pure-Python loops."""
+def visible(i, j, causal, window):
+    """Key j visible to query i: top-left causal mask and an optional
+    (left, right) window, either side None for unbounded."""
+    left, right = window if window is not None else (None, None)
+    if causal and j > i:
+        return False
+    if left is not None and j < i - left:
+        return False
+    if right is not None and j > i + right:
+        return False
+    return True
+
+
+def brute_force(q, k, v, causal, scale, window=None):
+    """q [Lq,d], k,v [Lk,d] -> O [Lq,d], LSE [Lq] with pure-Python loops.
+    A row with no visible key gets O = 0 and LSE = -inf."""
     Lq, d = q.shape
     Lk = k.shape[0]
     O = np.zeros((Lq, d))
     L = np.zeros(Lq)
     for i in range(Lq):
-        js = [j for j in range(Lk) if (not causal) or j <= i]
+        js = [j for j in range(Lk) if visible(i, j, causal, window)]
+        if not js:
+            L[i] = -math.inf
+            continue
         w = []
         for j in js:
             s = scale * math.fsum(float(q[i, t]) * float(k[j, t])
@@ -52,7 +69,7 @@ def brute_force(q, k, v, causal, scale):
     return O, L
 
 
-def online_blocked(q, k, v, causal, scale, block):
+def online_blocked(q, k, v, causal, scale, block, window=None):
     """Stream K/V in tiles of ``block`` keys with the online-softmax update.
 
     State per query row: running max M, running sum L, unnormalised output
@@ -69,8 +86,13 @@ def online_blocked(q, k, v, causal, scale, block):
     for j0 in range(0, Lk, block):
         j1 = min(Lk, j0 + block)
         S = (q @ k[j0:j1].T) * scale
+        cols = np.arange(j0, j1)[None, :]
         if causal:
-            S = np.where(np.arange(j0, j1)[None, :] <= rows, S, -np.inf)
+            S = np.where(cols <= rows, S, -np.inf)
+        if window is not None and window[0] is not None:
+            S = np.where(cols >= rows - window[0], S, -np.inf)
+        if window is not None and window[1] is not None:
+            S = np.where(cols <= rows + window[1], S, -np.inf)
         M_new = np.maximum(M, S.max(axis=1))
         safe = np.where(np.isneginf(M_new), 0.0, M_new)   # fully masked rows
         P = np.exp(S - safe[:, None])
@@ -78,7 +100,8 @@ def online_blocked(q, k, v, causal, scale, block):
         L = L * alpha + P.sum(axis=1)
         O = O * alpha[:, None] + P @ v[j0:j1]
         M = M_new
-    return O / L[:, None], M + np.log(L)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(L[:, None] > 0, O / np.where(L > 0, L, 1.0)[:, None], 0.0), M + np.log(L)
 
 
 def _parse_value(tok: str) -> float:

@@ -19,7 +19,10 @@ GOLDEN = Path(__file__).parent / "golden" / "hand_softmax_weights.txt"
 
 
 def _make_mutant(kind):
-    def chunk(q64, k64, v64, rows, causal, scale, want_p):
+    def chunk(q64, k64, v64, rows, causal, scale, want_p, window=None):
+        left, right = window if window is not None else (None, None)
+        if kind == "window_sides_swapped":
+            left, right = right, left
         Lk = k64.shape[0]
         ncols = Lk if not causal else min(Lk, int(rows.max()) + 1)
         if kind == "causal_plus_one":
@@ -41,6 +44,15 @@ def _make_mutant(kind):
                 allowed = cols <= rows[:, None]
         else:
             allowed = np.ones((len(rows), ncols), dtype=bool)
+        if left is not None:
+            if kind == "window_left_strict":
+                allowed = allowed & (cols > rows[:, None] - left)
+            elif kind == "window_left_plus_one":
+                allowed = allowed & (cols >= rows[:, None] - left - 1)
+            else:
+                allowed = allowed & (cols >= rows[:, None] - left)
+        if right is not None:
+            allowed = allowed & (cols <= rows[:, None] + right)
         sm = np.where(allowed, s, -np.inf)
         m = sm.max(axis=1)
         with np.errstate(invalid="ignore", divide="ignore"):
@@ -64,7 +76,8 @@ def _make_mutant(kind):
 
 MUTANTS = ["no_scale", "sign", "strict_causal", "causal_plus_one",
            "bottom_right", "column_normalise", "keys_as_values", "lse_log2",
-           "lse_no_max"]
+           "lse_no_max", "window_left_strict", "window_left_plus_one",
+           "window_sides_swapped"]
 
 
 def _pins_pass():
@@ -84,6 +97,13 @@ def _pins_pass():
                 Ob, Lb = brute_force(q[0, 0], k[0, 0], v[0, 0], causal, 0.7)
                 np.testing.assert_allclose(O[0, 0], Ob, atol=1e-12)
                 np.testing.assert_allclose(L[0, 0], Lb, atol=1e-12)
+        # sliding windows: left only (with causal), both sides, right only
+        for causal, window in ((True, (2, None)), (False, (1, 3)), (False, (None, 1))):
+            q, k, v = rng_qkv(2, 1, 1, 7, 7, 3)
+            O, L = attention_ref(q, k, v, causal, 0.7, window=window)
+            Ob, Lb = brute_force(q[0, 0], k[0, 0], v[0, 0], causal, 0.7, window)
+            np.testing.assert_allclose(O[0, 0], Ob, atol=1e-12)
+            np.testing.assert_allclose(L[0, 0], Lb, atol=1e-12)
     except AssertionError:
         return False
     return True

@@ -24,15 +24,21 @@ GOLDEN = Path(__file__).parent / "golden" / "hand_softmax_weights.txt"
 
 # --- hand-worked example -------------------------------------------------
 
-@pytest.mark.parametrize("case", ["noncausal", "causal", "rect_causal"])
+GOLDEN_CASES = {            # case -> (causal, window)
+    "noncausal": (False, None), "causal": (True, None), "rect_causal": (True, None),
+    "window_causal": (True, (1, None)), "band": (False, (1, 1)),
+}
+
+
+@pytest.mark.parametrize("case", list(GOLDEN_CASES))
 def test_golden_hand_example(case):
     g = golden_cases(GOLDEN)
     q, k, v, scale = g["q"], g["k"], g["v"], g["scale"]
     if case == "rect_causal":
         q = q[:2]
-    causal = case != "noncausal"
+    causal, window = GOLDEN_CASES[case]
     O, L = attention_ref(q[None, None], k[None, None], v[None, None],
-                         causal, scale)
+                         causal, scale, window=window)
     np.testing.assert_allclose(O[0, 0], g[f"{case} O"], rtol=0, atol=1e-12)
     np.testing.assert_allclose(L[0, 0], g[f"{case} LSE"], rtol=0, atol=1e-12)
 
@@ -234,3 +240,124 @@ def test_algorithmic_flops_closed_form():
     assert algorithmic_flops(np.arange(L), 700, d, False) == 4 * d * L * 700
     # causal with Lk < Lq: rows past Lk see all Lk keys
     assert algorithmic_flops(np.arange(10), 4, 2, True) == 4 * 2 * (1 + 2 + 3 + 4 * 7)
+
+
+# --- sliding window ("Flash Attention 原理与实现详解" (tbr8.org), section 6.3
+# "滑动窗口注意力": a (left, right) window-size pair, (1024, 0) with causal) --
+
+WINDOWS = [(True, (0, None)), (True, (3, None)), (False, (2, 2)),
+           (False, (None, 1)), (False, (4, 0)), (True, (1, 5))]
+
+
+@pytest.mark.parametrize("causal,window", WINDOWS)
+@pytest.mark.parametrize("Lq,Lk,d", [(9, 9, 3), (6, 11, 2), (12, 5, 4)])
+def test_window_brute_force(causal, window, Lq, Lk, d):
+    q, k, v = rng_qkv(21, 1, 2, Lq, Lk, d)
+    O, L = attention_ref(q, k, v, causal, 0.6, window=window)
+    for h in range(2):
+        Ob, Lb = brute_force(q[0, h], k[0, h], v[0, h], causal, 0.6, window)
+        np.testing.assert_allclose(O[0, h], Ob, rtol=0, atol=1e-13)
+        np.testing.assert_array_equal(np.isneginf(L[0, h]), np.isneginf(Lb))
+        fin = np.isfinite(Lb)
+        np.testing.assert_allclose(L[0, h][fin], Lb[fin], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal,window", WINDOWS)
+def test_window_sdpa_band_mask(causal, window):
+    """torch's fp64 SDPA with an explicit boolean band mask (rows that keep
+    at least one key; SDPA has no convention for empty rows)."""
+    import torch
+    import torch.nn.functional as F
+    Lq, Lk, d = 40, 52, 8
+    q, k, v = rng_qkv(22, 1, 2, Lq, Lk, d)
+    O, _ = attention_ref(q, k, v, causal, 0.3, window=window)
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lk)[None, :]
+    keep = np.ones((Lq, Lk), dtype=bool)
+    if causal:
+        keep &= j <= i
+    if window[0] is not None:
+        keep &= j >= i - window[0]
+    if window[1] is not None:
+        keep &= j <= i + window[1]
+    rows = keep.any(axis=1)
+    ref = F.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(keep), scale=0.3).numpy()
+    np.testing.assert_allclose(O[:, :, rows], ref[:, :, rows], rtol=0, atol=1e-12)
+
+
+def test_window_zero_is_identity():
+    """window (0, 0): each query sees only its own key: O_i = v_i and
+    LSE_i = scale q_i . k_i exactly."""
+    q, k, v = rng_qkv(23, 1, 1, 30, 30, 5)
+    O, L = attention_ref(q, k, v, False, 0.8, window=(0, 0))
+    np.testing.assert_allclose(O[0, 0], v[0, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(L[0, 0], 0.8 * np.einsum("id,id->i", q[0, 0], k[0, 0]),
+                               rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("left,right", [(3, 0), (5, 2), (None, 4), (0, None)])
+def test_window_scale_zero_band_means(left, right):
+    """scale 0: uniform weights over the band, O_i = mean of v over
+    [max(0, i-left), min(Lk-1, i+right)] and LSE_i = ln(count)."""
+    Lq, Lk = 20, 17
+    q, k, v = rng_qkv(24, 1, 1, Lq, Lk, 3)
+    O, L = attention_ref(q, k, v, False, 0.0, window=(left, right))
+    csum = np.concatenate([np.zeros((1, 3)), np.cumsum(v[0, 0], axis=0)])
+    for i in range(Lq):
+        lo = 0 if left is None else max(0, i - left)
+        hi = Lk - 1 if right is None else min(Lk - 1, i + right)
+        if hi < lo:
+            assert np.isneginf(L[0, 0, i]) and not O[0, 0, i].any()
+            continue
+        n = hi - lo + 1
+        np.testing.assert_allclose(O[0, 0, i], (csum[hi + 1] - csum[lo]) / n,
+                                   rtol=0, atol=1e-13)
+        assert abs(L[0, 0, i] - math.log(n)) < 1e-13
+
+
+def test_window_reduces_to_causal_and_full():
+    q, k, v = rng_qkv(25, 2, 2, 33, 33, 6)
+    Oc, Lc = attention_ref(q, k, v, True, 0.5)
+    Ow, Lw = attention_ref(q, k, v, False, 0.5, window=(None, 0))
+    np.testing.assert_allclose(Ow, Oc, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Lw, Lc, rtol=0, atol=1e-14)
+    Ow, Lw = attention_ref(q, k, v, True, 0.5, window=(33, None))
+    np.testing.assert_allclose(Ow, Oc, rtol=0, atol=1e-14)
+    Of, Lf = attention_ref(q, k, v, False, 0.5)
+    Ow, Lw = attention_ref(q, k, v, False, 0.5, window=(40, 40))
+    np.testing.assert_allclose(Ow, Of, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(Lw, Lf, rtol=0, atol=1e-14)
+
+
+def test_window_empty_rows():
+    """Lq > Lk with a left bound: rows i > Lk - 1 + left see no key; they
+    read O = 0 and LSE = -inf, every other row is finite."""
+    q, k, v = rng_qkv(26, 1, 1, 12, 4, 3)
+    O, L = attention_ref(q, k, v, True, 0.5, window=(2, None))
+    empty = np.arange(12) > 4 - 1 + 2
+    assert np.isneginf(L[0, 0, empty]).all() and not O[0, 0, empty].any()
+    assert np.isfinite(L[0, 0, ~empty]).all()
+
+
+@pytest.mark.parametrize("window", [(5, None), (7, 3), (None, 2)])
+@pytest.mark.parametrize("block", [1, 7, 16, 64])
+def test_window_online_recurrence(window, block):
+    causal = window[1] is None
+    q, k, v = rng_qkv(27, 1, 1, 70, 90, 8, sigma=2.0)
+    O, L = attention_ref(q, k, v, causal, 0.45, window=window)
+    Ob, Lb = online_blocked(q[0, 0], k[0, 0], v[0, 0], causal, 0.45, block, window)
+    np.testing.assert_allclose(Ob, O[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(Lb, L[0, 0], rtol=0, atol=1e-12)
+
+
+def test_window_algorithmic_flops_closed_form():
+    from oracle import algorithmic_flops
+    L, W, d = 1000, 100, 64
+    # causal, left window W: row i sees min(i, W) + 1 keys
+    pairs = sum(min(i, W) + 1 for i in range(L))
+    assert pairs == L * (W + 1) - W * (W + 1) // 2
+    assert algorithmic_flops(np.arange(L), L, d, True, (W, None)) == 4 * d * pairs
+    # window (0, 0): one pair per row that has a key
+    assert algorithmic_flops(np.arange(10), 6, d, False, (0, 0)) == 4 * d * 6
