@@ -74,12 +74,22 @@ def to_device(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
-def flops_of(w, causal: bool) -> float:
+def flops_of(w, causal: bool, window=None) -> float:
+    """4*d flops per visible (query, key) pair: exactly half the dense count
+    for the causal square workloads (the pages' benchmark convention), the
+    counted pairs for a sliding window (left, right; None = no bound)."""
     f = 4.0 * w.B * w.H * w.Lq * w.Lk * w.d
-    return f / 2 if causal else f
+    if window is None:
+        return f / 2 if causal else f
+    i = np.arange(w.Lq, dtype=np.int64)
+    hi = np.minimum(w.Lk - 1, i + window[1]) if window[1] is not None else np.full_like(i, w.Lk - 1)
+    lo = np.maximum(0, i - window[0]) if window[0] is not None else np.zeros_like(i)
+    pairs = int(np.maximum(hi - lo + 1, 0).sum())
+    return 4.0 * w.B * w.H * w.d * pairs
 
 
-def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None):
+def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
+                 window=None):
     """Time the oracle on whole (batch, head) slices of the workload, one
     after another, until ``budget_s`` of host time is spent or all slices
     are done.  Also reports the GPU result's error on that sample."""
@@ -90,18 +100,19 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None):
     slices = [(b, h) for b in range(w.B) for h in range(w.H)]
     if max_heads:
         slices = slices[:max_heads]
-    per_slice = algorithmic_flops(np.arange(w.Lq), w.Lk, w.d, causal)
+    per_slice = algorithmic_flops(np.arange(w.Lq), w.Lk, w.d, causal, window)
     spent, done, eo, el = 0.0, 0, 0.0, 0.0
     for b, h in slices:
         qs, ks, vs = (widen(x[b:b + 1, h:h + 1]) for x in (q, k, v))
         t0 = time.perf_counter()
         O_ref, L_ref = attention_ref(qs, ks, vs, causal, w.scale,
-                                     workers=cores, chunk=256)
+                                     workers=cores, chunk=256, window=window)
         spent += time.perf_counter() - t0
         done += 1
         eo = max(eo, float(np.abs(widen(O_gpu[b:b + 1, h:h + 1]) - O_ref).max()))
-        el = max(el, float(np.abs(L_gpu[b:b + 1, h:h + 1].astype(np.float64)
-                                  - L_ref).max()))
+        fin = np.isfinite(L_ref)
+        el = max(el, float(np.abs(L_gpu[b:b + 1, h:h + 1].astype(np.float64)[fin]
+                                  - L_ref[fin]).max()))
         if spent >= budget_s:
             break
     fl = done * per_slice
@@ -146,7 +157,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=["causal", "noncausal"], default=None,
+    ap.add_argument("--mode", choices=["causal", "noncausal", "window"], default=None,
                     help="default: the workload's first mode")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="host seconds for the CPU-baseline sample")
@@ -174,6 +185,7 @@ def main(argv=None):
     w = WORKLOADS[a.workload]
     mode = a.mode or w.modes[0]
     causal = mode == "causal"
+    window = w.window if mode == "window" else None
     log(f"bench: workload {w.name} mode {mode} steps {a.steps} warmup {a.warmup}")
     q, k, v = workload_inputs(w)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
@@ -181,9 +193,14 @@ def main(argv=None):
     od = torch.empty((w.B, w.H, w.Lq, w.d), dtype=tdt, device="cuda")
     ld = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
-    args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal),
-            w.scale, stream)
+    if window is not None:
+        fn = fa.fa_fwd_window
+        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, *w.window_abi,
+                w.scale, stream)
+    else:
+        fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal),
+                w.scale, stream)
 
     for _ in range(a.warmup):
         fn(*args)
@@ -201,7 +218,7 @@ def main(argv=None):
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]   # ms
     ms_kernel = float(np.mean(per))
     ms_step = wall * 1e3 / a.steps
-    flops = flops_of(w, causal)
+    flops = flops_of(w, causal, window)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -218,7 +235,7 @@ def main(argv=None):
         gpu_out = (o_np, ld.cpu().numpy())
         log("bench: CPU oracle baseline ...")
         cpu, parity = cpu_baseline(w, causal, q, k, v, gpu_out, a.cpu_budget,
-                                   a.cpu_heads)
+                                   a.cpu_heads, window)
         log(f"bench: oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores "
             f"-> {cpu['value'] * 1e3:.2f} GFLOP/s; parity on sample {parity}")
 
@@ -238,6 +255,7 @@ def main(argv=None):
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "config": {"workload": f"{w.name} ({mode})", "B": w.B, "H": w.H,
                    "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "causal": causal,
+                   "window": None if window is None else list(w.window_abi),
                    "scale": w.scale, "seed": w.seed,
                    "sigma_qk": w.sigma_qk, "sigma_v": w.sigma_v},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),

@@ -23,8 +23,8 @@ STATUS_NAMES = {
     4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_ARG", 7: "FA_ERR_LAUNCH",
 }
 # every function the C header declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_abi_version",
-           "fa_tile_config")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_status_string",
+           "fa_abi_version", "fa_tile_config")
 
 
 class FABuildError(RuntimeError):
@@ -56,6 +56,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_f32.argtypes = sig
     lib.fa_fwd_f32.restype = i
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_window.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -130,11 +132,27 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream=None):
                  causal, scale, stream)
 
 
+def fa_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, window_left, window_right,
+                  scale, stream=None):
+    """bf16 sliding-window forward through the C ABI (``fa_fwd_window``):
+    key j visible to query i iff i - window_left <= j <= i + window_right;
+    -1 leaves that side unbounded."""
+    st = load_library().fa_fwd_window(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Lq),
+        int(Lk), int(d), int(window_left), int(window_right), float(scale),
+        _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
+
+
 def attention(q, k, v, causal: bool = False, scale: float | None = None,
-              stream=None):
+              stream=None, window=None):
     """Convenience wrapper on torch tensors [B,H,L,d] (bf16 or fp32, on the
     GPU, contiguous): allocates O and LSE with torch and calls the C ABI on
-    ``stream`` (default: torch's current stream).  Returns (O, LSE)."""
+    ``stream`` (default: torch's current stream).  ``window``: optional
+    (left, right) sliding window, None on a side for no bound (bf16 only;
+    combined with ``causal`` the right bound is 0).  Returns (O, LSE)."""
     import torch
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, L, d]")
@@ -150,7 +168,15 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
         stream = torch.cuda.current_stream(q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    if q.dtype == torch.bfloat16:
+    if window is not None:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("sliding windows are implemented for bf16 only")
+        left = -1 if window[0] is None else int(window[0])
+        right = -1 if window[1] is None else int(window[1])
+        if causal:
+            right = 0 if right < 0 else min(right, 0)
+        fa_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, left, right, scale, stream)
+    elif q.dtype == torch.bfloat16:
         fa_fwd(q, k, v, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
     elif q.dtype == torch.float32:
         fa_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
@@ -159,6 +185,6 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
     return o, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "attention", "status_string",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_window", "attention", "status_string",
            "abi_version", "tile_config", "load_library", "FAError",
            "FABuildError", "EXPORTS", "LIB_PATH"]

@@ -4,6 +4,7 @@
 // nonzero status means nothing was enqueued.  The only HIP calls are the
 // kernel launch and hipGetLastError right after it.
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -24,10 +25,17 @@ bool overlaps(const void* p, std::size_t bytes, const void* r, std::size_t rbyte
     return a < b + rbytes && b < a + bytes;
 }
 
+// Which keys each query sees (after the ABI arguments are checked).
+struct MaskSpec {
+    bool causal = false;   // fa_fwd / fa_fwd_f32
+    bool window = false;   // fa_fwd_window with a bound the causal flag cannot express
+    int wl = 0, wr = 0;    // window bounds, clamped to [0, Lq + Lk]
+};
+
 int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
                         const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int Lq, int Lk, int d, int causal,
-                        float scale, hipStream_t stream) {
+                        int B, int H, int Lq, int Lk, int d, int mask_status,
+                        const MaskSpec& mask, float scale, hipStream_t stream) {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
     fa::TileConfig tc;
@@ -36,7 +44,7 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         !aligned16(lse))
         return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
-    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    if (mask_status != FA_OK) return mask_status;   // causal / window arguments
 
     // sizes: element counts must fit the kernel's 64-bit offsets and the
     // per-head int arithmetic; the grid must fit one dimension.
@@ -55,9 +63,35 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         overlaps(lse, lbytes, o, qbytes))
         return FA_ERR_ARG;
 
-    const hipError_t err = fa::launch_fwd(dt, q, k, v, o, lse, B, H, Lq, Lk, d,
-                                          causal == 1, scale, stream);
+    const hipError_t err =
+        mask.window ? fa::launch_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, mask.wl, mask.wr,
+                                            scale, stream)
+                    : fa::launch_fwd(dt, q, k, v, o, lse, B, H, Lq, Lk, d, mask.causal, scale,
+                                     stream);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// causal flag of fa_fwd / fa_fwd_f32
+int causal_mask(int causal, MaskSpec* m) {
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    m->causal = causal == 1;
+    return FA_OK;
+}
+
+// window pair of fa_fwd_window: -1 = unbounded on that side.  (-1, -1) is
+// full attention and (-1, 0) the causal mask; both take those kernels.
+int window_mask(int left, int right, int Lq, int Lk, MaskSpec* m) {
+    if (left < -1 || right < -1) return FA_ERR_ARG;
+    const long long cap = (long long)Lq + Lk;   // farther bounds change nothing
+    if (left == -1 && right == -1) return FA_OK;
+    if (left == -1 && right == 0) {
+        m->causal = true;
+        return FA_OK;
+    }
+    m->window = true;
+    m->wl = (int)(left < 0 ? cap : std::min<long long>(left, cap));
+    m->wr = (int)(right < 0 ? cap : std::min<long long>(right, cap));
+    return FA_OK;
 }
 
 }  // namespace
@@ -67,15 +101,28 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Lq, int Lk, int d, int causal, float scale,
            hipStream_t stream) {
+    MaskSpec m;
+    const int ms = causal_mask(causal, &m);
     return validate_and_launch(fa::DType::BF16, 2, q, k, v, o, lse, B, H, Lq,
-                               Lk, d, causal, scale, stream);
+                               Lk, d, ms, m, scale, stream);
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                float* lse, int B, int H, int Lq, int Lk, int d, int causal,
                float scale, hipStream_t stream) {
+    MaskSpec m;
+    const int ms = causal_mask(causal, &m);
     return validate_and_launch(fa::DType::F32, 4, q, k, v, o, lse, B, H, Lq,
-                               Lk, d, causal, scale, stream);
+                               Lk, d, ms, m, scale, stream);
+}
+
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Lq, int Lk, int d, int window_left, int window_right,
+                  float scale, hipStream_t stream) {
+    MaskSpec m;
+    const int ms = window_mask(window_left, window_right, Lq, Lk, &m);
+    return validate_and_launch(fa::DType::BF16, 2, q, k, v, o, lse, B, H, Lq,
+                               Lk, d, ms, m, scale, stream);
 }
 
 const char* fa_status_string(int status) {
@@ -86,7 +133,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED_D: return "head dim d must be 64, 128 or 256";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_ARG: return "causal must be 0 or 1 and outputs must not overlap inputs";
+    case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, and outputs must not overlap inputs";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     default: return "unknown status";
     }

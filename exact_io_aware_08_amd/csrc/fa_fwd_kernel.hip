@@ -542,13 +542,22 @@ template <int D> struct DGeom {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
 
-template <int D, bool CAUSAL>
+// Which keys a query sees: all of them, the causal prefix j <= i (top-left),
+// or a sliding window i - wl <= j <= i + wr (the window-size pair of
+// "Flash Attention 原理与实现详解" (tbr8.org), section 6.3 "滑动窗口注意力";
+// (wl, 0) is a causal window).  Always also j < Lk.
+enum Mask : int { kFull = 0, kCausal = 1, kWindow = 2 };
+
+template <int D, int MASK>
 __global__ __launch_bounds__((DGeom<D>::NT))
 __attribute__((amdgpu_waves_per_eu(DGeom<D>::WPE, DGeom<D>::WPE)))
 void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-                          float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c)
+                          float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c,
+                          int wl, int wr)
 {
+    constexpr bool CAUSAL = MASK == kCausal;
+    constexpr bool WINDOW = MASK == kWindow;
     using G = DGeom<D>;
     using E = BF16;
     using Frag = bf16x8;
@@ -611,8 +620,12 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         l_run[nb] = 0.f;
     }
 
-    const int kv_end = CAUSAL ? min(Lk, q0 + BM) : Lk;
-    const int nt = (kv_end + BN - 1) / BN;
+    // key tiles [jlo, nt) hold every key a row of this block may see
+    const int kv_end = CAUSAL ? min(Lk, q0 + BM) : WINDOW ? min(Lk, q0 + BM + wr) : Lk;
+    // (clamped to the last tile: a block whose rows all lie past Lk - 1 + wl
+    // still visits one tile, fully masked, so its rows come out empty)
+    const int jlo = WINDOW ? min(max(0, q0 - wl), Lk - 1) / BN : 0;
+    const int nt = max((kv_end + BN - 1) / BN, jlo + 1);
 
     // ---- tile copy: HBM -> LDS, no registers ------------------------------
     // Per-lane parts of the copy addresses (element offsets inside a tile):
@@ -636,7 +649,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // it, so every step issues the same copies without branches and the
     // counted waits below stay exact.
     auto issue_k = [&](int j, uint16_t* Kd) {
-        const int kv0 = min(j, nt - 1) * BN;
+        const int kv0 = min(j, nt - 1) * BN;   // j >= jlo
         const uint16_t* Kt = Kh + (size_t)kv0 * D;   // wave-uniform tile base
         const int last = Lk - 1 - kv0;
 #pragma unroll
@@ -725,15 +738,31 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // used by the exponentials and sets alpha
     auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha) {
         const int qb0 = q0w + 32 * nb;
-        if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > qb0)) {
+        // some key of the tile lies past Lk, right of a row's last key, or
+        // (window) left of a row's first key
+        if ((kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > qb0) ||
+            (WINDOW && (kv0 + BN - 1 > qb0 + wr || kv0 < qb0 + 31 - wl))) {
+            // This lane's query sees keys kb + e for e in [lo, lo + span],
+            // where element i of key block mb is e = mb*32 + i.  One
+            // unsigned compare per element; an empty range gets lo past
+            // the tile.  The scheduling barrier after each key block keeps
+            // the compiler from hoisting all 64 compare masks into SGPRs.
             const int qi = qb0 + col;
+            const int kb = kv0 + 16 * half;
+            int hi = Lk - 1;
+            if (CAUSAL) hi = min(hi, qi);
+            if (WINDOW) hi = min(hi, qi + wr);
+            hi = min(hi - kb, BN);
+            int lo = WINDOW ? max(qi - wl - kb, 0) : 0;
+            unsigned span = (unsigned)(hi - lo);
+            if (hi < lo) { lo = BN + 1; span = 0u; }
 #pragma unroll
-            for (int mb = 0; mb < NMB; ++mb)
+            for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kj = kv0 + mb * 32 + 16 * half + i;
-                    if ((kj >= Lk) || (CAUSAL && kj > qi)) sacc[mb][i] = -__builtin_inff();
-                }
+                for (int i = 0; i < 16; ++i)
+                    if ((unsigned)(mb * 32 + i - lo) > span) sacc[mb][i] = -__builtin_inff();
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // NMB independent 3-input chains, then combined
         float pm[NMB];
@@ -834,7 +863,9 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int kv0 = j * BN;
         issue_k(j + 1, Kn);
         issue_v(j + 1, Vn);
-        if (!CAUSAL || kv0 <= qlast_w) {
+        // waves whose rows see no key of this tile skip its math
+        if ((!CAUSAL || kv0 <= qlast_w) &&
+            (!WINDOW || (kv0 <= qlast_w + wr && kv0 + BN - 1 >= q0w - wl))) {
             f32x16 sacc[NBQ][NMB];
             s_tile(Kc, sacc);
             float alpha[NBQ], rs[NBQ];
@@ -851,10 +882,10 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
         sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
     };
-    issue_k(0, Kb0);
-    issue_v(0, Vb0);
+    issue_k(jlo, Kb0);
+    issue_v(jlo, Vb0);
     sync_after(InFlight0{});
-    for (int j = 0; j < nt; j += 2) {
+    for (int j = jlo; j < nt; j += 2) {
         step(j, Kb0, Vb0, Kb1, Vb1);
         if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
     }
@@ -865,7 +896,9 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
         const float lt = half_sum(l_run[nb]);
-        const float inv = 1.0f / lt;
+        // a window can leave a row (i > Lk - 1 + wl) with no key: O = 0 and
+        // LSE = -inf (log of an empty sum)
+        const float inv = (!WINDOW || lt > 0.f) ? 1.0f / lt : 0.f;
         const int row = q0w + 32 * nb + col;
         if (row < Lq) {
 #pragma unroll
@@ -878,23 +911,38 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                     E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
                 }
             if (half == 0)
-                LSE[(size_t)bh * Lq + row] = (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2;
+                LSE[(size_t)bh * Lq + row] = (!WINDOW || lt > 0.f)
+                    ? (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
         }
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 hipError_t launch_direct(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int B, int H, int Lq, int Lk, float scale, hipStream_t stream)
+                         int B, int H, int Lq, int Lk, float scale, int wl, int wr,
+                         hipStream_t stream)
 {
     using G = DGeom<D>;
     const int BH = B * H;
     const int nqb = (Lq + G::BM - 1) / G::BM;
-    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(G::NT),
+    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(G::NT),
                        0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq, Lk,
-                       nqb, scale * kLog2e);
+                       nqb, scale * kLog2e, wl, wr);
     return hipGetLastError();
+}
+
+template <int MASK>
+hipError_t launch_direct_d(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Lq, int Lk, int d, float scale, int wl, int wr,
+                           hipStream_t stream)
+{
+    switch (d) {
+    case 64:  return launch_direct<64, MASK>(q, k, v, o, lse, B, H, Lq, Lk, scale, wl, wr, stream);
+    case 128: return launch_direct<128, MASK>(q, k, v, o, lse, B, H, Lq, Lk, scale, wl, wr, stream);
+    case 256: return launch_direct<256, MASK>(q, k, v, o, lse, B, H, Lq, Lk, scale, wl, wr, stream);
+    default:  return hipErrorInvalidValue;
+    }
 }
 
 template <class E, int D, bool CAUSAL>
@@ -932,15 +980,8 @@ hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
 {
 #ifndef FA_NO_DIRECT
     if constexpr (std::is_same<E, BF16>::value) {
-        if (d == 64)
-            return causal ? launch_direct<64, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
-                          : launch_direct<64, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
-        if (d == 128)
-            return causal ? launch_direct<128, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
-                          : launch_direct<128, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
-        if (d == 256)
-            return causal ? launch_direct<256, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream)
-                          : launch_direct<256, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
+        return causal ? launch_direct_d<kCausal>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream)
+                      : launch_direct_d<kFull>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream);
     }
 #endif
     switch (d) {
@@ -989,6 +1030,13 @@ hipError_t launch_fwd(DType dt, const void* q, const void* k, const void* v,
     if (dt == DType::BF16)
         return launch_e<BF16>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
     return launch_e<F32>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
+}
+
+hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Lq, int Lk, int d, int wl, int wr, float scale,
+                             hipStream_t stream)
+{
+    return launch_direct_d<kWindow>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, wl, wr, stream);
 }
 
 }  // namespace fa

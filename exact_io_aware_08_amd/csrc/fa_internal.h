@@ -24,4 +24,10 @@ hipError_t launch_fwd(DType dt, const void* q, const void* k, const void* v,
                       void* o, float* lse, int B, int H, int Lq, int Lk,
                       int d, bool causal, float scale, hipStream_t stream);
 
+// bf16 sliding window: key j visible to query i iff i - wl <= j <= i + wr
+// (and j < Lk); wl, wr >= 0, already clamped to at most Lq + Lk.
+hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Lq, int Lk, int d, int wl, int wr, float scale,
+                             hipStream_t stream);
+
 }  // namespace fa

@@ -2,12 +2,13 @@
  * fa.h - C ABI of the MI355X (gfx950) FlashAttention-2 forward library
  *        (libfa_fwd.so).
  *
- * Operation (both entry points):  for every batch b < B, head h < H and
- * query row i < Lq,
+ * Operation (all three forward entry points):  for every batch b < B,
+ * head h < H and query row i < Lq,
  *
  *     s_ij   = scale * sum_t q[b,h,i,t] * k[b,h,j,t]        j < Lk
  *     A_i    = { j < Lk }                  (causal == 0)
  *            = { j < Lk : j <= i }         (causal == 1, top-left aligned)
+ *            = { j < Lk : i - wl <= j <= i + wr }    (fa_fwd_window)
  *     o[b,h,i,:] = sum_{j in A_i} softmax_j(s_i.) * v[b,h,j,:]
  *     lse[b,h,i] = ln( sum_{j in A_i} exp(s_ij) )           natural log
  *
@@ -46,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2   /* 2: fa_fwd_window added */
 
 enum fa_status {
     FA_OK = 0,
@@ -55,7 +56,8 @@ enum fa_status {
     FA_ERR_UNSUPPORTED_D = 3,  /* d is not 64, 128 or 256                    */
     FA_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned           */
     FA_ERR_SCALE = 5,          /* scale is not finite and > 0                */
-    FA_ERR_ARG = 6,            /* causal not 0/1, or outputs overlap inputs  */
+    FA_ERR_ARG = 6,            /* causal not 0/1, a window bound < -1, or
+                                  outputs overlap inputs                     */
     FA_ERR_LAUNCH = 7          /* the kernel launch failed                   */
 };
 
@@ -83,6 +85,23 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                float* lse, int B, int H, int Lq, int Lk, int d, int causal,
                float scale, hipStream_t stream);
+
+/*
+ * bf16 sliding-window forward: key j is visible to query i iff
+ * i - window_left <= j <= i + window_right (and j < Lk), the (left, right)
+ * window-size pair of "Flash Attention 原理与实现详解" (tbr8.org), section
+ * 6.3 "滑动窗口注意力" ((1024, 0) together with causal masking: 1024 keys to
+ * the left of each query and none to its right).  A bound of -1 means no
+ * bound on that side, so (-1, 0) is fa_fwd with causal = 1 and (-1, -1) is
+ * fa_fwd with causal = 0; a bound w >= 0 admits keys at distance up to and
+ * including w.  A query row with no visible key (only possible when
+ * i > Lk - 1 + window_left) gets o = 0 and lse = -inf.  Other arguments,
+ * layout, ownership, precision and errors as fa_fwd; a bound below -1 is
+ * FA_ERR_ARG.  Only tiles that intersect a query block's band are read.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Lq, int Lk, int d, int window_left,
+                  int window_right, float scale, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -27,10 +27,16 @@ class Workload:
     Lk: int
     d: int
     dtype: str            # "bf16" or "fp32"
-    modes: tuple          # subset of ("noncausal", "causal")
+    modes: tuple          # subset of ("noncausal", "causal", "window")
     seed: int
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
+    window: tuple | None = None   # (left, right), None for no bound
+
+    @property
+    def window_abi(self) -> tuple:
+        """The window as fa_fwd_window takes it: -1 for no bound."""
+        return tuple(-1 if w is None else int(w) for w in self.window)
 
     @property
     def scale(self) -> float:
@@ -51,6 +57,12 @@ WORKLOADS = {
     "bf16_peaky_d256_ragged": Workload("bf16_peaky_d256_ragged", 1, 8, 8000,
                                        8192, 256, "bf16", ("noncausal",), 5,
                                        sigma_qk=3.0),
+    # sliding window of 1024 keys to the left and none to the right, the
+    # pages' example window ("Flash Attention 原理与实现详解" (tbr8.org),
+    # section 6.3), at the 16K causal shape
+    "bf16_window1k_16k_d128": Workload("bf16_window1k_16k_d128", 1, 16, 16384,
+                                       16384, 128, "bf16", ("window",), 6,
+                                       window=(1024, 0)),
 }
 
 

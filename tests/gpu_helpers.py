@@ -31,12 +31,14 @@ def to_device(x: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
 
 
-def run_fa(q, k, v, causal: bool, scale: float, stream=None, guard=True):
+def run_fa(q, k, v, causal: bool, scale: float, stream=None, guard=True,
+           window=None):
     """Run the HIP forward on storage arrays (uint16 bf16 bits or fp32).
 
-    Outputs are allocated with GUARD canary elements on both sides; the
-    canaries are checked after the call.  Returns (O storage array, LSE
-    float32 array)."""
+    ``window``: (left, right) with -1 for no bound; calls fa_fwd_window
+    (``causal`` is then ignored).  Outputs are allocated with GUARD canary
+    elements on both sides; the canaries are checked after the call.
+    Returns (O storage array, LSE float32 array)."""
     import torch
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
@@ -57,8 +59,12 @@ def run_fa(q, k, v, causal: bool, scale: float, stream=None, guard=True):
     lse = lbuf[g:g + n_l]
     if stream is None:
         stream = torch.cuda.current_stream()
-    fn = fa.fa_fwd if bf16 else fa.fa_fwd_f32
-    fn(qd, kd, vd, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
+    if window is not None:
+        fa.fa_fwd_window(qd, kd, vd, o, lse, B, H, Lq, Lk, d, int(window[0]),
+                         int(window[1]), scale, stream)
+    else:
+        fn = fa.fa_fwd if bf16 else fa.fa_fwd_f32
+        fn(qd, kd, vd, o, lse, B, H, Lq, Lk, d, int(causal), scale, stream)
     torch.cuda.synchronize()
     ob = obuf.cpu().numpy()
     lb = lbuf.cpu().numpy()
@@ -77,12 +83,18 @@ def run_fa(q, k, v, causal: bool, scale: float, stream=None, guard=True):
 
 
 def check_parity(O, LSE, O_ref, LSE_ref, dtype: str, label: str = ""):
-    """Assert the stated bar; return the measured errors."""
+    """Assert the stated bar; return the measured errors.  Rows the oracle
+    leaves empty (LSE = -inf, O = 0: only sliding windows make them) must
+    be exactly that on the GPU too; the bar applies to the other rows."""
     Og = widen(O)
     assert np.isfinite(Og).all(), f"{label}: non-finite O"
+    empty = np.isneginf(LSE_ref)
+    assert (np.isneginf(LSE) == empty).all(), f"{label}: empty rows differ"
+    assert not Og[empty].any(), f"{label}: O of an empty row is not 0"
+    LSE, LSE_ref = LSE[~empty], LSE_ref[~empty]
     assert np.isfinite(LSE).all(), f"{label}: non-finite LSE"
     eo = float(np.abs(Og - O_ref).max())
-    el = float(np.abs(LSE.astype(np.float64) - LSE_ref).max())
+    el = float(np.abs(LSE.astype(np.float64) - LSE_ref).max()) if LSE.size else 0.0
     if dtype == "bf16":
         say(f"{label}: max|dO|={eo:.3e} (bar {BF16_O_ATOL}) "
             f"max|dLSE|={el:.3e} (bar {BF16_LSE_ATOL})")

@@ -95,3 +95,25 @@ def test_validation_errors(fn):
     assert _st(fn, lse=O + 16) == 6
     # a grid too large for one dimension
     assert _st(fn, B=1 << 16, H=1 << 15, Lq=1 << 20) == 2
+
+
+def _st_window(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Lq=128, Lk=128, d=64,
+                window_left=16, window_right=0, scale=0.125)
+    args.update(kw)
+    try:
+        fa.fa_fwd_window(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+def test_window_validation_errors():
+    assert _st_window(q=0) == 1
+    assert _st_window(Lk=0) == 2
+    assert _st_window(d=96) == 3
+    assert _st_window(v=V + 4) == 4
+    assert _st_window(scale=math.nan) == 5
+    for wl, wr in ((-2, 0), (0, -2), (-5, -5)):
+        assert _st_window(window_left=wl, window_right=wr) == 6
+    assert _st_window(o=K + 64) == 6

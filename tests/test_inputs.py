@@ -42,7 +42,9 @@ def test_sigma_and_widen():
 
 
 def test_workload_table():
-    assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5]
+    assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5, 6]
+    w = WORKLOADS["bf16_window1k_16k_d128"]
+    assert w.window == (1024, 0) and w.window_abi == (1024, 0) and w.modes == ("window",)
     w = WORKLOADS["bf16_peaky_d256_ragged"]
     assert (w.Lq, w.Lk, w.d, w.sigma_qk) == (8000, 8192, 256, 3.0)
     assert np.float32(WORKLOADS["bf16_4k_d128"].scale) == np.float32(1 / np.sqrt(np.float32(128)))
