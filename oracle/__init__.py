@@ -3,6 +3,7 @@
 Only the tests, the package smoke check and the bench's CPU-baseline leg
 may import this package.  The product path never does.
 """
-from .attention_fp64 import attention_ref, default_workers, algorithmic_flops
+from .attention_fp64 import (algorithmic_flops, attention_ref, default_workers,
+                             merge_partials)
 
-__all__ = ["attention_ref", "default_workers", "algorithmic_flops"]
+__all__ = ["attention_ref", "merge_partials", "default_workers", "algorithmic_flops"]

@@ -58,17 +58,19 @@ except Exception:  # pragma: no cover
     threadpool_limits = None
 
 
-def _chunk_ref(q64, k64, v64, rows, causal, scale, want_p, window=None):
+def _chunk_ref(q64, k64, v64, rows, causal, scale, want_p, window=None,
+               keys=None):
     """One (b, h, row-chunk): q64 [R, d] rows at absolute indices ``rows``."""
     left, right = window if window is not None else (None, None)
     Lk = k64.shape[0]
+    k_lo, k_hi = keys if keys is not None else (0, Lk)
     # columns that any row of this chunk may see
-    hi = Lk
+    hi = min(Lk, k_hi)
     if causal:
         hi = min(hi, int(rows.max()) + 1)
     if right is not None:
         hi = min(hi, int(rows.max()) + right + 1)
-    lo = 0 if left is None else max(0, int(rows.min()) - left)
+    lo = k_lo if left is None else max(k_lo, int(rows.min()) - left)
     hi = max(hi, lo)
     cols = np.arange(lo, hi)
     s = (q64 @ k64[lo:hi].T) * scale                         # step 1
@@ -96,7 +98,7 @@ def _chunk_ref(q64, k64, v64, rows, causal, scale, want_p, window=None):
 
 def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
                   return_p: bool = False, workers: int | None = None,
-                  chunk: int = 512, window=None):
+                  chunk: int = 512, window=None, keys=None):
     """fp64 attention forward.
 
     q: [B, H, Lq, d]; k, v: [B, H, Lk, d]; any real dtype (widened exactly
@@ -107,6 +109,9 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
 
     ``window``: optional (left, right) sliding window; each entry a
     non-negative int or None (no bound on that side).
+    ``keys``: optional (k0, k1): only keys k0 <= j < k1 take part (the
+    partial result of one key split; rows left empty read O = 0,
+    LSE = -inf).
 
     Returns O [B, H, R, d] and LSE [B, H, R] in fp64 (R = Lq or len(rows)),
     plus P [B, H, R, Lk] when ``return_p``.
@@ -140,7 +145,7 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
         b, h, c0, c1 = job
         r = rows[c0:c1]
         o, lse, p = _chunk_ref(q[b, h, r], k[b, h], v[b, h], r, causal,
-                               scale, return_p, window)
+                               scale, return_p, window, keys)
         O[b, h, c0:c1] = o
         LSE[b, h, c0:c1] = lse
         if return_p:
@@ -164,6 +169,40 @@ def attention_ref(q, k, v, causal: bool, scale: float, *, rows=None,
     if return_p:
         return O, LSE, P
     return O, LSE
+
+
+def merge_partials(O_parts, LSE_parts):
+    """Combine partial results over disjoint key sets into the result over
+    their union: the block-merge step of "Flash Attention 原理与实现详解"
+    (tbr8.org), section 2.1 "Tiling（分块计算）策略" -- with running max m,
+    sum l and unnormalised output O, merging a block (m_b, l_b, O_b) gives
+    m' = max(m, m_b), O' = O e^(m - m') + O_b e^(m_b - m'),
+    l' = l e^(m - m') + l_b e^(m_b - m').  A normalised partial
+    (O_s, LSE_s) is the state m = LSE_s, l = 1, O = O_s, so folding the
+    partials in one after another and dividing by l at the end gives
+    O = sum_s e^(LSE_s - LSE) O_s and LSE = m + ln l.
+
+    O_parts [S, ..., d], LSE_parts [S, ...] (fp64).  Partials with
+    LSE_s = -inf (no key of the set visible) contribute nothing; if every
+    partial is empty the row is empty (O = 0, LSE = -inf).
+    """
+    O_parts = np.asarray(O_parts, dtype=np.float64)
+    LSE_parts = np.asarray(LSE_parts, dtype=np.float64)
+    m = np.full(LSE_parts.shape[1:], -np.inf)
+    l = np.zeros(LSE_parts.shape[1:])
+    O = np.zeros(O_parts.shape[1:])
+    with np.errstate(invalid="ignore"):
+        for O_b, m_b in zip(O_parts, LSE_parts):
+            m_new = np.maximum(m, m_b)
+            safe = np.where(np.isneginf(m_new), 0.0, m_new)
+            a = np.exp(m - safe)        # 0 where m = -inf
+            b = np.exp(m_b - safe)      # 0 where m_b = -inf
+            O = O * a[..., None] + O_b * b[..., None]
+            l = l * a + b
+            m = m_new
+    with np.errstate(divide="ignore", invalid="ignore"):
+        O = np.where(l[..., None] > 0, O / np.where(l > 0, l, 1.0)[..., None], 0.0)
+        return O, m + np.log(l)
 
 
 def default_workers() -> int:
@@ -193,4 +232,4 @@ def algorithmic_flops(Lq_rows, Lk: int, d: int, causal: bool, window=None) -> fl
     return float(4.0 * d * vis.sum())
 
 
-__all__ = ["attention_ref", "default_workers", "algorithmic_flops"]
+__all__ = ["attention_ref", "merge_partials", "default_workers", "algorithmic_flops"]

@@ -19,7 +19,7 @@ GOLDEN = Path(__file__).parent / "golden" / "hand_softmax_weights.txt"
 
 
 def _make_mutant(kind):
-    def chunk(q64, k64, v64, rows, causal, scale, want_p, window=None):
+    def chunk(q64, k64, v64, rows, causal, scale, want_p, window=None, keys=None):
         left, right = window if window is not None else (None, None)
         if kind == "window_sides_swapped":
             left, right = right, left

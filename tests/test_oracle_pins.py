@@ -361,3 +361,62 @@ def test_window_algorithmic_flops_closed_form():
     assert algorithmic_flops(np.arange(L), L, d, True, (W, None)) == 4 * d * pairs
     # window (0, 0): one pair per row that has a key
     assert algorithmic_flops(np.arange(10), 6, d, False, (0, 0)) == 4 * d * 6
+
+
+# --- key splits and their merge ("Flash Attention 原理与实现详解" (tbr8.org),
+# section 2.1 "Tiling（分块计算）策略", the block-merge step) ------------------
+
+def _split_points(Lk, splits, rng):
+    cuts = np.sort(rng.choice(np.arange(1, Lk), size=splits - 1, replace=False))
+    return [0, *cuts.tolist(), Lk]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_merge_of_key_splits_equals_full(causal, splits):
+    """Partials over disjoint key ranges, merged, give the full result; for
+    causal rows some ranges are empty (LSE = -inf) and must drop out."""
+    from oracle import merge_partials
+    q, k, v = rng_qkv(40 + splits, 1, 2, 37, 53, 6, sigma=1.5)
+    O, L = attention_ref(q, k, v, causal, 0.4)
+    cut = _split_points(53, splits, np.random.default_rng(splits))
+    parts = [attention_ref(q, k, v, causal, 0.4, keys=(a, b))
+             for a, b in zip(cut[:-1], cut[1:])]
+    Om, Lm = merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_allclose(Om, O, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Lm, L, rtol=0, atol=1e-13)
+
+
+def test_key_range_partial_is_attention_over_that_range():
+    """A partial is plain attention over the keys of its range (brute force
+    on the sliced K and V), and a row with no key in range is empty."""
+    q, k, v = rng_qkv(44, 1, 1, 9, 12, 3)
+    O, L = attention_ref(q, k, v, True, 0.9, keys=(4, 10))
+    for i in range(9):
+        js = [j for j in range(4, 10) if j <= i]
+        if not js:
+            assert np.isneginf(L[0, 0, i]) and not O[0, 0, i].any()
+            continue
+        Ob, Lb = brute_force(q[0, 0, i:i + 1], k[0, 0, js], v[0, 0, js], False, 0.9)
+        np.testing.assert_allclose(O[0, 0, i], Ob[0], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(L[0, 0, i], Lb[0], rtol=0, atol=1e-13)
+
+
+def test_merge_lse_is_logsumexp_and_order_free():
+    from scipy.special import logsumexp
+    from oracle import merge_partials
+    rng = np.random.default_rng(45)
+    Op = rng.standard_normal((5, 2, 3, 4))
+    Lp = rng.standard_normal((5, 2, 3)) * 4
+    Lp[1, 0, 0] = -np.inf                      # an empty partial
+    Om, Lm = merge_partials(Op, Lp)
+    np.testing.assert_allclose(Lm, logsumexp(Lp, axis=0), rtol=0, atol=1e-13)
+    w = np.exp(Lp - Lm[None])
+    np.testing.assert_allclose(Om, (w[..., None] * Op).sum(axis=0), rtol=0, atol=1e-13)
+    perm = [3, 0, 4, 2, 1]
+    Op2, Lp2 = merge_partials(Op[perm], Lp[perm])
+    np.testing.assert_allclose(Op2, Om, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Lp2, Lm, rtol=0, atol=1e-13)
+    # all partials empty: the row is empty
+    Oe, Le = merge_partials(np.zeros((3, 1, 2)), np.full((3, 1), -np.inf))
+    assert np.isneginf(Le).all() and not Oe.any()
