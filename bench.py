@@ -157,7 +157,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=["causal", "noncausal", "window"], default=None,
+    ap.add_argument("--mode", choices=["causal", "noncausal", "window", "splitkv"], default=None,
                     help="default: the workload's first mode")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="host seconds for the CPU-baseline sample")
@@ -193,10 +193,17 @@ def main(argv=None):
     od = torch.empty((w.B, w.H, w.Lq, w.d), dtype=tdt, device="cuda")
     ld = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+    splits = w.splits if mode == "splitkv" else 0
     if window is not None:
         fn = fa.fa_fwd_window
         args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, *w.window_abi,
                 w.scale, stream)
+    elif splits:
+        nbytes = fa.splitkv_workspace_size(w.B, w.H, w.Lq, w.d, splits)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")   # caller-owned scratch
+        fn = fa.fa_fwd_splitkv
+        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, 0, w.scale, splits,
+                ws, nbytes, stream)
     else:
         fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
         args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal),
@@ -225,6 +232,23 @@ def main(argv=None):
     log(f"bench: kernel {ms_kernel:.4f} ms (min {min(per):.4f}, median "
         f"{float(np.median(per)):.4f}), step {ms_step:.4f} ms, "
         f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.2f}% of {peak} peak")
+
+    unsplit_ms = None
+    if splits:
+        # the same inputs through the unsplit kernel, for reference
+        ref_args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, 0, w.scale, stream)
+        for _ in range(2):
+            fa.fa_fwd(*ref_args)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fa.fa_fwd(*ref_args)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        unsplit_ms = e0.elapsed_time(e1) / 10
+        log(f"bench: unsplit fa_fwd on the same inputs {unsplit_ms:.4f} ms")
+        fn(*args)   # leave the split result in od / ld for the CPU check
+        torch.cuda.synchronize()
 
     gpu_out = None
     cpu = None
@@ -256,6 +280,7 @@ def main(argv=None):
         "config": {"workload": f"{w.name} ({mode})", "B": w.B, "H": w.H,
                    "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "causal": causal,
                    "window": None if window is None else list(w.window_abi),
+                   "num_splits": splits or None,
                    "scale": w.scale, "seed": w.seed,
                    "sigma_qk": w.sigma_qk, "sigma_v": w.sigma_v},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
@@ -269,6 +294,8 @@ def main(argv=None):
     }
     if parity is not None:
         line["parity_on_cpu_sample"] = parity
+    if unsplit_ms is not None:
+        line["unsplit_kernel_ms"] = round(unsplit_ms, 5)
     print(json.dumps(line), flush=True)
     return 0
 

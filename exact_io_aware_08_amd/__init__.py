@@ -21,10 +21,12 @@ FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED_D",
     4: "FA_ERR_ALIGN", 5: "FA_ERR_SCALE", 6: "FA_ERR_ARG", 7: "FA_ERR_LAUNCH",
+    8: "FA_ERR_WORKSPACE",
 }
 # every function the C header declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_status_string",
-           "fa_abi_version", "fa_tile_config")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
+           "fa_splitkv_workspace_size", "fa_status_string", "fa_abi_version",
+           "fa_tile_config")
 
 
 class FABuildError(RuntimeError):
@@ -58,6 +60,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_f32.restype = i
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_window.restype = i
+    sz = ctypes.c_size_t
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_fwd_splitkv.restype = i
+    lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_splitkv_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -146,13 +153,36 @@ def fa_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, window_left, window_right,
     return st
 
 
+def splitkv_workspace_size(B, H, Lq, d, num_splits) -> int:
+    """Bytes of workspace fa_fwd_splitkv needs (0: invalid arguments)."""
+    return int(load_library().fa_splitkv_workspace_size(int(B), int(H), int(Lq),
+                                                         int(d), int(num_splits)))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, num_splits,
+                   workspace, workspace_bytes, stream=None):
+    """bf16 key-split forward through the C ABI (``fa_fwd_splitkv``):
+    ``num_splits`` partial results in the caller's ``workspace`` (device
+    pointer or tensor of at least ``splitkv_workspace_size`` bytes), then
+    their merge into o and lse."""
+    st = load_library().fa_fwd_splitkv(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Lq),
+        int(Lk), int(d), int(causal), float(scale), int(num_splits), _ptr(workspace),
+        int(workspace_bytes), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
+
+
 def attention(q, k, v, causal: bool = False, scale: float | None = None,
-              stream=None, window=None):
+              stream=None, window=None, num_splits: int | None = None):
     """Convenience wrapper on torch tensors [B,H,L,d] (bf16 or fp32, on the
     GPU, contiguous): allocates O and LSE with torch and calls the C ABI on
     ``stream`` (default: torch's current stream).  ``window``: optional
     (left, right) sliding window, None on a side for no bound (bf16 only;
-    combined with ``causal`` the right bound is 0).  Returns (O, LSE)."""
+    combined with ``causal`` the right bound is 0).  ``num_splits``: split
+    the keys among that many workgroups per query block and merge (bf16
+    only; the workspace is allocated with torch).  Returns (O, LSE)."""
     import torch
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, L, d]")
@@ -168,7 +198,16 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
         stream = torch.cuda.current_stream(q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    if window is not None:
+    if num_splits is not None:
+        if q.dtype != torch.bfloat16 or window is not None:
+            raise ValueError("key splits are implemented for bf16 without a window")
+        nbytes = splitkv_workspace_size(B, H, Lq, d, num_splits)
+        if nbytes == 0:
+            raise ValueError(f"unsupported num_splits {num_splits}")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, int(causal), scale,
+                       num_splits, ws, nbytes, stream)
+    elif window is not None:
         if q.dtype != torch.bfloat16:
             raise ValueError("sliding windows are implemented for bf16 only")
         left = -1 if window[0] is None else int(window[0])
@@ -185,6 +224,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
     return o, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_window", "attention", "status_string",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
+           "splitkv_workspace_size", "attention", "status_string",
            "abi_version", "tile_config", "load_library", "FAError",
            "FABuildError", "EXPORTS", "LIB_PATH"]

@@ -25,11 +25,26 @@ bool overlaps(const void* p, std::size_t bytes, const void* r, std::size_t rbyte
     return a < b + rbytes && b < a + bytes;
 }
 
+// Workspace of fa_fwd_splitkv: fp32 partial O [nsplit][B*H][Lq][d], then
+// fp32 partial LSE [nsplit][B*H][Lq], each part starting on 256 bytes.
+std::size_t round256(std::size_t n) { return (n + 255) & ~(std::size_t)255; }
+std::size_t split_opart_bytes(long long bh, int Lq, int d, int nsplit) {
+    return round256((std::size_t)nsplit * bh * Lq * d * sizeof(float));
+}
+std::size_t split_workspace_bytes(long long bh, int Lq, int d, int nsplit) {
+    return split_opart_bytes(bh, Lq, d, nsplit) +
+           round256((std::size_t)nsplit * bh * Lq * sizeof(float));
+}
+constexpr int kMaxSplits = 64;
+
 // Which keys each query sees (after the ABI arguments are checked).
 struct MaskSpec {
     bool causal = false;   // fa_fwd / fa_fwd_f32
     bool window = false;   // fa_fwd_window with a bound the causal flag cannot express
     int wl = 0, wr = 0;    // window bounds, clamped to [0, Lq + Lk]
+    int nsplit = 0;        // fa_fwd_splitkv: key splits (>= 1), else 0
+    void* workspace = nullptr;
+    std::size_t workspace_bytes = 0;
 };
 
 int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
@@ -44,7 +59,11 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         !aligned16(lse))
         return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
-    if (mask_status != FA_OK) return mask_status;   // causal / window arguments
+    if (mask_status != FA_OK) return mask_status;   // causal / window / split arguments
+    if (mask.nsplit) {
+        if (!mask.workspace) return FA_ERR_NULL;
+        if (!aligned16(mask.workspace)) return FA_ERR_ALIGN;
+    }
 
     // sizes: element counts must fit the kernel's 64-bit offsets and the
     // per-head int arithmetic; the grid must fit one dimension.
@@ -62,6 +81,22 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
         overlaps(lse, lbytes, o, qbytes))
         return FA_ERR_ARG;
+    if (mask.nsplit) {
+        const std::size_t wbytes = split_workspace_bytes(bh, Lq, d, mask.nsplit);
+        if (mask.workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+        const void* w = mask.workspace;
+        if (overlaps(w, wbytes, q, qbytes) || overlaps(w, wbytes, k, kbytes) ||
+            overlaps(w, wbytes, v, kbytes) || overlaps(w, wbytes, o, qbytes) ||
+            overlaps(w, wbytes, lse, lbytes))
+            return FA_ERR_ARG;
+        float* opart = static_cast<float*>(mask.workspace);
+        float* lpart = reinterpret_cast<float*>(static_cast<char*>(mask.workspace) +
+                                                split_opart_bytes(bh, Lq, d, mask.nsplit));
+        const hipError_t err = fa::launch_fwd_split(q, k, v, o, lse, B, H, Lq, Lk, d,
+                                                    mask.causal, scale, mask.nsplit, opart,
+                                                    lpart, stream);
+        return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    }
 
     const hipError_t err =
         mask.window ? fa::launch_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, mask.wl, mask.wr,
@@ -116,6 +151,26 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                                Lk, d, ms, m, scale, stream);
 }
 
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Lq, int Lk, int d, int causal, float scale,
+                   int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+    MaskSpec m;
+    int ms = causal_mask(causal, &m);
+    if (ms == FA_OK && (num_splits < 1 || num_splits > kMaxSplits)) ms = FA_ERR_ARG;
+    m.nsplit = num_splits;
+    m.workspace = workspace;
+    m.workspace_bytes = workspace_bytes;
+    return validate_and_launch(fa::DType::BF16, 2, q, k, v, o, lse, B, H, Lq,
+                               Lk, d, ms, m, scale, stream);
+}
+
+size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits) {
+    if (B < 1 || H < 1 || Lq < 1 || num_splits < 1 || num_splits > kMaxSplits) return 0;
+    if (d != 64 && d != 128 && d != 256) return 0;
+    return split_workspace_bytes((long long)B * H, Lq, d, num_splits);
+}
+
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Lq, int Lk, int d, int window_left, int window_right,
                   float scale, hipStream_t stream) {
@@ -133,8 +188,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED_D: return "head dim d must be 64, 128 or 256";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
-    case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, and outputs must not overlap inputs";
+    case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, 1 <= num_splits <= 64, and outputs and workspace must not overlap inputs";
     case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size";
     default: return "unknown status";
     }
 }

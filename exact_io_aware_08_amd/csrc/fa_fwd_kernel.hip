@@ -548,13 +548,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // (wl, 0) is a causal window).  Always also j < Lk.
 enum Mask : int { kFull = 0, kCausal = 1, kWindow = 2 };
 
-template <int D, int MASK>
+// SPLIT: the key tiles a query block visits are divided among nsplit
+// workgroups; each writes its partial result over its share, normalised,
+// in fp32 (Opart [nsplit][BH][Lq][D], Lpart [nsplit][BH][Lq], natural-log
+// LSE, O = 0 and LSE = -inf for a row that sees no key of the share), and
+// fa_merge_kernel combines the shares.
+template <int D, int MASK, bool SPLIT>
 __global__ __launch_bounds__((DGeom<D>::NT))
 __attribute__((amdgpu_waves_per_eu(DGeom<D>::WPE, DGeom<D>::WPE)))
 void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c,
-                          int wl, int wr)
+                          int wl, int wr, int nsplit, float* __restrict__ Opart,
+                          float* __restrict__ Lpart)
 {
     constexpr bool CAUSAL = MASK == kCausal;
     constexpr bool WINDOW = MASK == kWindow;
@@ -579,17 +585,23 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // Workgroups are dispatched round-robin over the 8 XCDs, so block id p
     // runs on XCD p % 8; every query block of a head goes to one XCD (its L2
     // serves the K/V re-reads) and, causal, the longest rows start first.
-    int bh, lvl;
+    // With key splits, each (head, split) pair counts as one head here.
+    int bh, lvl, split = 0;
     {
         const int p = blockIdx.x;
-        if ((BH & 7) == 0) {
-            const int own = BH >> 3;
+        const int BHS = SPLIT ? BH * nsplit : BH;
+        if ((BHS & 7) == 0) {
+            const int own = BHS >> 3;
             const int slot = p >> 3;
             bh = (p & 7) + 8 * (slot % own);
             lvl = slot / own;
         } else {
-            bh = p % BH;
-            lvl = p / BH;
+            bh = p % BHS;
+            lvl = p / BHS;
+        }
+        if (SPLIT) {
+            split = bh % nsplit;
+            bh /= nsplit;
         }
     }
     const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
@@ -624,8 +636,33 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     const int kv_end = CAUSAL ? min(Lk, q0 + BM) : WINDOW ? min(Lk, q0 + BM + wr) : Lk;
     // (clamped to the last tile: a block whose rows all lie past Lk - 1 + wl
     // still visits one tile, fully masked, so its rows come out empty)
-    const int jlo = WINDOW ? min(max(0, q0 - wl), Lk - 1) / BN : 0;
-    const int nt = max((kv_end + BN - 1) / BN, jlo + 1);
+    int jlo = WINDOW ? min(max(0, q0 - wl), Lk - 1) / BN : 0;
+    int nt = max((kv_end + BN - 1) / BN, jlo + 1);
+    if (SPLIT) {
+        // this split's share of the block's tiles; an empty share writes
+        // empty partial rows and leaves before any copy or barrier (the
+        // branch is the same for the whole workgroup)
+        const int per = (nt - jlo + nsplit - 1) / nsplit;
+        const int js = jlo + split * per;
+        const int je = min(nt, js + per);
+        if (js >= je) {
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                const int row = q0w + 32 * nb + col;
+                if (row >= Lq) continue;
+                float* Op = Opart + (((size_t)split * BH + bh) * Lq + row) * D;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<f32x4*>(Op + db * 32 + 8 * g + 4 * half) = f32x4{};
+                if (half == 0) Lpart[((size_t)split * BH + bh) * Lq + row] = -__builtin_inff();
+            }
+            return;
+        }
+        jlo = js;
+        nt = je;
+    }
 
     // ---- tile copy: HBM -> LDS, no registers ------------------------------
     // Per-lane parts of the copy addresses (element offsets inside a tile):
@@ -896,11 +933,25 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
         const float lt = half_sum(l_run[nb]);
-        // a window can leave a row (i > Lk - 1 + wl) with no key: O = 0 and
+        // a window or a key split can leave a row with no key: O = 0 and
         // LSE = -inf (log of an empty sum)
-        const float inv = (!WINDOW || lt > 0.f) ? 1.0f / lt : 0.f;
+        constexpr bool MAY_BE_EMPTY = WINDOW || SPLIT;
+        const float inv = (!MAY_BE_EMPTY || lt > 0.f) ? 1.0f / lt : 0.f;
         const int row = q0w + 32 * nb + col;
-        if (row < Lq) {
+        if (SPLIT && row < Lq) {
+            float* Op = Opart + (((size_t)split * BH + bh) * Lq + row) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v4 = {oacc[nb][db][4 * g + 0], oacc[nb][db][4 * g + 1],
+                                oacc[nb][db][4 * g + 2], oacc[nb][db][4 * g + 3]};
+                    *reinterpret_cast<f32x4*>(Op + db * 32 + 8 * g + 4 * half) = v4 * inv;
+                }
+            if (half == 0)
+                Lpart[((size_t)split * BH + bh) * Lq + row] =
+                    lt > 0.f ? (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
+        } else if (row < Lq) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -911,7 +962,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                     E::store4(Oh + (size_t)row * D + db * 32 + 8 * g + 4 * half, v4);
                 }
             if (half == 0)
-                LSE[(size_t)bh * Lq + row] = (!WINDOW || lt > 0.f)
+                LSE[(size_t)bh * Lq + row] = (!MAY_BE_EMPTY || lt > 0.f)
                     ? (m_run[nb] + __builtin_amdgcn_logf(lt)) * kLn2 : -__builtin_inff();
         }
     }
@@ -925,10 +976,64 @@ hipError_t launch_direct(const void* q, const void* k, const void* v, void* o, f
     using G = DGeom<D>;
     const int BH = B * H;
     const int nqb = (Lq + G::BM - 1) / G::BM;
-    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(G::NT),
-                       0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq, Lk,
-                       nqb, scale * kLog2e, wl, wr);
+    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, false>), dim3((unsigned)(nqb * BH)),
+                       dim3(G::NT), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<uint16_t*>(o), lse, BH, Lq, Lk, nqb, scale * kLog2e, wl, wr,
+                       1, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+// ---- merge of key-split partials ------------------------------------------
+// Block-merge step of "Flash Attention 原理与实现详解" (tbr8.org), section 2.1
+// "Tiling（分块计算）策略", applied to normalised partials (O_s, LSE_s):
+// LSE = m + ln(sum_s e^(LSE_s - m)), O = sum_s e^(LSE_s - m) O_s / sum_s
+// e^(LSE_s - m) with m = max_s LSE_s.  One thread per 4 elements of a row;
+// rows with every partial empty stay empty (O = 0, LSE = -inf).
+template <int D>
+__global__ __launch_bounds__(256)
+void fa_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart,
+                     uint16_t* __restrict__ O, float* __restrict__ LSE, int rows, int nsplit)
+{
+    constexpr int TPR = D / 4;              // threads per row
+    const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int c4 = (threadIdx.x % TPR) * 4;
+    if (row >= rows) return;
+    const size_t stride_o = (size_t)rows * D;
+    float m = -__builtin_inff();
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, Lpart[(size_t)s * rows + row]);
+    const float m_use = (m == -__builtin_inff()) ? 0.f : m;
+    f32x4 acc = {};
+    float l = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float w = __builtin_amdgcn_exp2f((Lpart[(size_t)s * rows + row] - m_use) * kLog2e);
+        l += w;
+        acc += w * *reinterpret_cast<const f32x4*>(Opart + s * stride_o + (size_t)row * D + c4);
+    }
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    BF16::store4(O + (size_t)row * D + c4, acc * inv);
+    if (c4 == 0) LSE[row] = l > 0.f ? m_use + __builtin_amdgcn_logf(l) * kLn2 : -__builtin_inff();
+}
+
+template <int D, int MASK>
+hipError_t launch_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int Lq, int Lk, float scale, int nsplit, float* opart,
+                        float* lpart, hipStream_t stream)
+{
+    using G = DGeom<D>;
+    const int BH = B * H;
+    const int nqb = (Lq + G::BM - 1) / G::BM;
+    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, true>),
+                       dim3((unsigned)(nqb * BH * nsplit)), dim3(G::NT), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq,
+                       Lk, nqb, scale * kLog2e, 0, 0, nsplit, opart, lpart);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int rows = BH * Lq;
+    constexpr int RPB = 256 / (D / 4);     // rows per merge block
+    hipLaunchKernelGGL((fa_merge_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, stream, opart, lpart, static_cast<uint16_t*>(o), lse, rows, nsplit);
     return hipGetLastError();
 }
 
@@ -1037,6 +1142,25 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
                              hipStream_t stream)
 {
     return launch_direct_d<kWindow>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, wl, wr, stream);
+}
+
+hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Lq, int Lk, int d, bool causal, float scale,
+                            int nsplit, float* opart, float* lpart, hipStream_t stream)
+{
+    switch (d) {
+    case 64:
+        return causal ? launch_split<64, kCausal>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream)
+                      : launch_split<64, kFull>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream);
+    case 128:
+        return causal ? launch_split<128, kCausal>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream)
+                      : launch_split<128, kFull>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream);
+    case 256:
+        return causal ? launch_split<256, kCausal>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream)
+                      : launch_split<256, kFull>(q, k, v, o, lse, B, H, Lq, Lk, scale, nsplit, opart, lpart, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fa

@@ -30,4 +30,11 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
                              int B, int H, int Lq, int Lk, int d, int wl, int wr, float scale,
                              hipStream_t stream);
 
+// bf16 key-split forward: nsplit partial results in fp32 (opart
+// [nsplit][B*H][Lq][d], lpart [nsplit][B*H][Lq]) then their merge into o and
+// lse; two kernels on `stream`.
+hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int Lq, int Lk, int d, bool causal, float scale,
+                            int nsplit, float* opart, float* lpart, hipStream_t stream);
+
 }  // namespace fa

@@ -2,7 +2,7 @@
  * fa.h - C ABI of the MI355X (gfx950) FlashAttention-2 forward library
  *        (libfa_fwd.so).
  *
- * Operation (all three forward entry points):  for every batch b < B,
+ * Operation (every forward entry point):  for every batch b < B,
  * head h < H and query row i < Lq,
  *
  *     s_ij   = scale * sum_t q[b,h,i,t] * k[b,h,j,t]        j < Lk
@@ -41,13 +41,15 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2   /* 2: fa_fwd_window added */
+#define FA_ABI_VERSION 3   /* 2: fa_fwd_window; 3: fa_fwd_splitkv */
 
 enum fa_status {
     FA_OK = 0,
@@ -58,7 +60,8 @@ enum fa_status {
     FA_ERR_SCALE = 5,          /* scale is not finite and > 0                */
     FA_ERR_ARG = 6,            /* causal not 0/1, a window bound < -1, or
                                   outputs overlap inputs                     */
-    FA_ERR_LAUNCH = 7          /* the kernel launch failed                   */
+    FA_ERR_LAUNCH = 7,         /* the kernel launch failed                   */
+    FA_ERR_WORKSPACE = 8       /* workspace smaller than required            */
 };
 
 /*
@@ -102,6 +105,37 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Lq, int Lk, int d, int window_left,
                   int window_right, float scale, hipStream_t stream);
+
+/*
+ * bf16 forward with the keys split among num_splits workgroups per query
+ * block, for shapes with too few query blocks to fill the GPU (short Lq,
+ * long Lk).  Each split computes the normalised partial result over its
+ * share of the block's key tiles, in fp32, into `workspace`; a second
+ * kernel merges the partials with the block-merge step of "Flash Attention
+ * 原理与实现详解" (tbr8.org), section 2.1 "Tiling（分块计算）策略":
+ * LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  The result
+ * is the same quantity as fa_fwd's (rounding differs only in the order of
+ * the sums).
+ *   num_splits      : 1 .. 64
+ *   workspace       : device memory of at least
+ *                     fa_splitkv_workspace_size(B, H, Lq, d, num_splits)
+ *                     bytes, 16-byte aligned, owned by the caller, not
+ *                     overlapping any other argument; its contents are
+ *                     scratch (overwritten, need not be initialised).
+ *                     Concurrent calls need separate workspaces.
+ * Both kernels are enqueued on `stream`.  Other arguments, layout,
+ * ownership and errors as fa_fwd; a NULL workspace is FA_ERR_NULL, a
+ * misaligned one FA_ERR_ALIGN, num_splits out of range FA_ERR_ARG, a small
+ * one FA_ERR_WORKSPACE.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Lq, int Lk, int d, int causal, float scale,
+                   int num_splits, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/* Workspace bytes fa_fwd_splitkv needs, or 0 for invalid arguments
+ * (B, H, Lq < 1, d not 64/128/256, num_splits outside 1 .. 64).  Host-only. */
+size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

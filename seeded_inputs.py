@@ -27,11 +27,12 @@ class Workload:
     Lk: int
     d: int
     dtype: str            # "bf16" or "fp32"
-    modes: tuple          # subset of ("noncausal", "causal", "window")
+    modes: tuple          # subset of ("noncausal", "causal", "window", "splitkv")
     seed: int
     sigma_qk: float = 1.0
     sigma_v: float = 1.0
     window: tuple | None = None   # (left, right), None for no bound
+    splits: int = 0               # key splits for the "splitkv" mode
 
     @property
     def window_abi(self) -> tuple:
@@ -63,6 +64,11 @@ WORKLOADS = {
     "bf16_window1k_16k_d128": Workload("bf16_window1k_16k_d128", 1, 16, 16384,
                                        16384, 128, "bf16", ("window",), 6,
                                        window=(1024, 0)),
+    # short queries against a long key sequence: 2 query blocks per head,
+    # too few workgroups for 256 CUs unless the keys are split
+    "bf16_longkv_512x64k_d128": Workload("bf16_longkv_512x64k_d128", 1, 16, 512,
+                                         65536, 128, "bf16", ("splitkv",), 7,
+                                         splits=16),
 }
 
 

@@ -49,8 +49,8 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for st in range(8):
-        assert fa.status_string(st)
+    for st in range(9):
+        assert fa.status_string(st) != "unknown status"
     assert fa.status_string(99) == "unknown status"
 
 
@@ -117,3 +117,41 @@ def test_window_validation_errors():
     for wl, wr in ((-2, 0), (0, -2), (-5, -5)):
         assert _st_window(window_left=wl, window_right=wr) == 6
     assert _st_window(o=K + 64) == 6
+
+
+W = 0x10000000 * 7   # fake workspace address, disjoint from the others
+
+
+def _st_split(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Lq=128, Lk=128, d=64,
+                causal=0, scale=0.125, num_splits=4, workspace=W,
+                workspace_bytes=1 << 30)
+    args.update(kw)
+    try:
+        fa.fa_fwd_splitkv(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+def test_splitkv_workspace_size():
+    # fp32 partial O then fp32 partial LSE, each rounded up to 256 bytes
+    def r(n):
+        return (n + 255) // 256 * 256
+    for (B, H, Lq, d, S) in ((1, 2, 128, 64, 4), (2, 3, 77, 128, 7), (1, 1, 1, 256, 1)):
+        assert fa.splitkv_workspace_size(B, H, Lq, d, S) == \
+            r(S * B * H * Lq * d * 4) + r(S * B * H * Lq * 4)
+    for bad in ((0, 1, 8, 64, 2), (1, 1, 8, 96, 2), (1, 1, 8, 64, 0), (1, 1, 8, 64, 65)):
+        assert fa.splitkv_workspace_size(*bad) == 0
+
+
+def test_splitkv_validation_errors():
+    assert _st_split(workspace=0) == 1
+    assert _st_split(workspace=W + 8) == 4
+    assert _st_split(causal=3) == 6
+    for n in (0, -1, 65):
+        assert _st_split(num_splits=n) == 6
+    need = fa.splitkv_workspace_size(1, 2, 128, 64, 4)
+    assert _st_split(workspace_bytes=need - 1) == 8
+    assert _st_split(workspace=Q + 256) == 6         # overlaps q
+    assert _st_split(d=32) == 3
