@@ -65,10 +65,11 @@ WORKLOADS = {
                                        16384, 128, "bf16", ("window",), 6,
                                        window=(1024, 0)),
     # short queries against a long key sequence: 2 query blocks per head,
-    # too few workgroups for 256 CUs unless the keys are split
+    # too few workgroups for 256 CUs unless the keys are split (8 splits:
+    # 256 workgroups, the fastest of 1..64 measured)
     "bf16_longkv_512x64k_d128": Workload("bf16_longkv_512x64k_d128", 1, 16, 512,
                                          65536, 128, "bf16", ("splitkv",), 7,
-                                         splits=16),
+                                         splits=8),
 }
 
 

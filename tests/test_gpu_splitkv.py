@@ -114,7 +114,7 @@ def test_splitkv_matches_unsplit_kernel():
 
 def test_longkv_workload_sampled():
     """The bench's long-key workload (B=1, H=16, Lq=512, Lk=65536, d=128,
-    16 splits) at full size, checked on sampled rows."""
+    8 splits) at full size, checked on sampled rows."""
     w = WORKLOADS["bf16_longkv_512x64k_d128"]
     q, k, v = workload_inputs(w)
     rows = sample_rows(w.Lq, 256, 24, 43)

@@ -43,7 +43,7 @@ def test_sigma_and_widen():
 
 def test_workload_table():
     assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5, 6, 7]
-    assert WORKLOADS["bf16_longkv_512x64k_d128"].splits == 16
+    assert WORKLOADS["bf16_longkv_512x64k_d128"].splits == 8
     w = WORKLOADS["bf16_window1k_16k_d128"]
     assert w.window == (1024, 0) and w.window_abi == (1024, 0) and w.modes == ("window",)
     w = WORKLOADS["bf16_peaky_d256_ragged"]
