@@ -129,6 +129,38 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
     }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "slices": done}
 
 
+def cpu_baseline_bwd(w, causal, q, k, v, do, grads, budget_s=15.0, max_heads=None):
+    """Time the fp64 backward oracle on whole (batch, head) slices until
+    ``budget_s`` of host time is spent; report the GPU gradients' error on
+    that sample relative to each tensor's largest magnitude."""
+    from oracle import attention_bwd_ref, backward_flops, default_workers
+    from seeded_inputs import widen
+    cores = default_workers()
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if max_heads:
+        slices = slices[:max_heads]
+    spent, done, rel = 0.0, 0, [0.0, 0.0, 0.0]
+    for b, h in slices:
+        xs = [widen(x[b:b + 1, h:h + 1]) for x in (q, k, v, do)]
+        t0 = time.perf_counter()
+        ref = attention_bwd_ref(*xs, causal, w.scale)
+        spent += time.perf_counter() - t0
+        done += 1
+        for n, (g, r) in enumerate(zip(grads, ref)):
+            gr = widen(g[b:b + 1, h:h + 1])
+            rel[n] = max(rel[n], float(np.abs(gr - r).max() / np.abs(r).max()))
+        if spent >= budget_s:
+            break
+    fl = done * backward_flops(w.Lq, w.Lk, w.d, causal)
+    return {
+        "value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": (f"{done} of {w.B * w.H} (batch, head) slices, full backward each, "
+                   f"fp64 numpy oracle (BLAS threads per numpy default), {spent:.2f} s wall"),
+        "seconds": spent,
+    }, {"max_rel_err_dQ": rel[0], "max_rel_err_dK": rel[1], "max_rel_err_dV": rel[2],
+        "slices": done}
+
+
 def copy_calibration(mib: int, steps: int, warmup: int) -> int:
     """Plain copy of a known byte count: reads and writes mib MiB per step."""
     import torch
@@ -157,7 +189,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=["causal", "noncausal", "window", "splitkv"], default=None,
+    ap.add_argument("--mode", choices=["causal", "noncausal", "window", "splitkv", "bwd"],
+                    default=None,
                     help="default: the workload's first mode")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="host seconds for the CPU-baseline sample")
@@ -184,7 +217,7 @@ def main(argv=None):
 
     w = WORKLOADS[a.workload]
     mode = a.mode or w.modes[0]
-    causal = mode == "causal"
+    causal = mode == "causal" or (mode == "bwd" and "causal" in w.modes)
     window = w.window if mode == "window" else None
     log(f"bench: workload {w.name} mode {mode} steps {a.steps} warmup {a.warmup}")
     q, k, v = workload_inputs(w)
@@ -194,7 +227,24 @@ def main(argv=None):
     ld = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     splits = w.splits if mode == "splitkv" else 0
-    if window is not None:
+    backward = mode == "bwd"
+    if backward:
+        if w.dtype != "bf16":
+            raise SystemExit("the backward is bf16 only")
+        from seeded_inputs import make_grad
+        do = make_grad(w.seed, w.B, w.H, w.Lq, w.d)
+        dod = to_device(do)
+        # the forward's O and LSE, computed once outside the timed region
+        fa.fa_fwd(qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal), w.scale, stream)
+        dqd = torch.empty_like(od)
+        dkd = torch.empty((w.B, w.H, w.Lk, w.d), dtype=torch.bfloat16, device="cuda")
+        dvd = torch.empty_like(dkd)
+        nbytes = fa.bwd_workspace_size(w.B, w.H, w.Lq)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")   # caller-owned scratch
+        fn = fa.fa_bwd
+        args = (qd, kd, vd, od, ld, dod, dqd, dkd, dvd, w.B, w.H, w.Lq, w.Lk, w.d,
+                int(causal), w.scale, ws, nbytes, stream)
+    elif window is not None:
         fn = fa.fa_fwd_window
         args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, *w.window_abi,
                 w.scale, stream)
@@ -226,6 +276,8 @@ def main(argv=None):
     ms_kernel = float(np.mean(per))
     ms_step = wall * 1e3 / a.steps
     flops = flops_of(w, causal, window)
+    if backward:
+        flops *= 2.5   # the pages' count: 2.0 (backward) + 0.5 (recomputed S, P)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -253,7 +305,13 @@ def main(argv=None):
     gpu_out = None
     cpu = None
     parity = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and backward:
+        grads = [t.view(torch.int16).cpu().numpy().view(np.uint16) for t in (dqd, dkd, dvd)]
+        log("bench: CPU oracle baseline (backward) ...")
+        cpu, parity = cpu_baseline_bwd(w, causal, q, k, v, do, grads, a.cpu_budget, a.cpu_heads)
+        log(f"bench: oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores "
+            f"-> {cpu['value'] * 1e3:.2f} GFLOP/s; parity on sample {parity}")
+    elif not a.no_cpu_baseline:
         o_np = od.view(torch.int16).cpu().numpy().view(np.uint16) \
             if w.dtype == "bf16" else od.cpu().numpy()
         gpu_out = (o_np, ld.cpu().numpy())
@@ -280,7 +338,7 @@ def main(argv=None):
         "config": {"workload": f"{w.name} ({mode})", "B": w.B, "H": w.H,
                    "Lq": w.Lq, "Lk": w.Lk, "d": w.d, "causal": causal,
                    "window": None if window is None else list(w.window_abi),
-                   "num_splits": splits or None,
+                   "num_splits": splits or None, "pass": "backward" if backward else "forward",
                    "scale": w.scale, "seed": w.seed,
                    "sigma_qk": w.sigma_qk, "sigma_v": w.sigma_v},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),

@@ -25,8 +25,8 @@ STATUS_NAMES = {
 }
 # every function the C header declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
-           "fa_splitkv_workspace_size", "fa_status_string", "fa_abi_version",
-           "fa_tile_config")
+           "fa_splitkv_workspace_size", "fa_bwd", "fa_bwd_workspace_size",
+           "fa_status_string", "fa_abi_version", "fa_tile_config")
 
 
 class FABuildError(RuntimeError):
@@ -65,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
@@ -174,6 +178,24 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, num_splits,
     return st
 
 
+def bwd_workspace_size(B, H, Lq) -> int:
+    """Bytes of workspace fa_bwd needs (0: invalid arguments)."""
+    return int(load_library().fa_bwd_workspace_size(int(B), int(H), int(Lq)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, causal, scale,
+           workspace, workspace_bytes, stream=None):
+    """bf16 backward through the C ABI (``fa_bwd``): dq, dk, dv from q, k,
+    v, the forward's o and lse, and the upstream gradient dout."""
+    st = load_library().fa_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+        _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), int(causal), float(scale),
+        _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
+
+
 def attention(q, k, v, causal: bool = False, scale: float | None = None,
               stream=None, window=None, num_splits: int | None = None):
     """Convenience wrapper on torch tensors [B,H,L,d] (bf16 or fp32, on the
@@ -225,6 +247,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
 
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
-           "splitkv_workspace_size", "attention", "status_string",
+           "splitkv_workspace_size", "fa_bwd", "bwd_workspace_size", "attention",
+           "status_string",
            "abi_version", "tile_config", "load_library", "FAError",
            "FABuildError", "EXPORTS", "LIB_PATH"]

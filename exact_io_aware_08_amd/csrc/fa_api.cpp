@@ -5,6 +5,7 @@
 // kernel launch and hipGetLastError right after it.
 
 #include <algorithm>
+#include <initializer_list>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -129,6 +130,11 @@ int window_mask(int left, int right, int Lq, int Lk, MaskSpec* m) {
     return FA_OK;
 }
 
+// Workspace of fa_bwd: Delta then LSE * log2(e), [B*H][Lq] fp32 each.
+std::size_t bwd_workspace_bytes(long long bh, int Lq) {
+    return 2 * round256((std::size_t)bh * Lq * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +184,52 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     const int ms = window_mask(window_left, window_right, Lq, Lk, &m);
     return validate_and_launch(fa::DType::BF16, 2, q, k, v, o, lse, B, H, Lq,
                                Lk, d, ms, m, scale, stream);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int Lq) {
+    if (B < 1 || H < 1 || Lq < 1) return 0;
+    return bwd_workspace_bytes((long long)B * H, Lq);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
+           int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+           hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+        return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+    if (!fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED_D;
+    for (const void* p : {q, k, v, o, static_cast<const void*>(lse), dout,
+                          static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv), static_cast<const void*>(workspace)})
+        if (!aligned16(p)) return FA_ERR_ALIGN;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    const long long bh = (long long)B * H;
+    if (bh > (1LL << 30) || (long long)Lq * d > 0x7fffffffLL || (long long)Lk * d > 0x7fffffffLL ||
+        bh * ((Lq + 255) / 256) > 0x7fffffffLL || bh * ((Lk + 127) / 128) > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
+    const std::size_t qbytes = (std::size_t)bh * Lq * d * 2;
+    const std::size_t kbytes = (std::size_t)bh * Lk * d * 2;
+    const std::size_t lbytes = (std::size_t)bh * Lq * sizeof(float);
+    const std::size_t wbytes = bwd_workspace_bytes(bh, Lq);
+    if (workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
+    // outputs (dq, dk, dv, workspace) must not overlap any argument or each other
+    struct Span { const void* p; std::size_t n; };
+    const Span ins[] = {{q, qbytes}, {k, kbytes}, {v, kbytes}, {o, qbytes}, {lse, lbytes},
+                        {dout, qbytes}};
+    const Span outs[] = {{dq, qbytes}, {dk, kbytes}, {dv, kbytes}, {workspace, wbytes}};
+    for (int i = 0; i < 4; ++i) {
+        for (const Span& s : ins)
+            if (overlaps(outs[i].p, outs[i].n, s.p, s.n)) return FA_ERR_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_ARG;
+    }
+    float* delta = static_cast<float*>(workspace);
+    float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wbytes / 2);
+    const hipError_t err = fa::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d,
+                                          causal == 1, scale, delta, lse2, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 const char* fa_status_string(int status) {

@@ -1,0 +1,512 @@
+// FlashAttention-2 backward kernels for gfx950 (MI355X, CDNA4), bf16.
+//
+// Gradients of sum(dO * O) for O = softmax(scale Q K^T) V, following "第 08 章:
+// Flash Attention——分块注意力" (chuoer47.github.io), section 6 "反向":
+//   Delta_i = sum_d dO_id O_id                                  (6.2)
+//   P_ij    = exp(scale q_i.k_j - LSE_i)   recomputed from the forward's LSE
+//   dV = P^T dO,  dP = dO V^T,  dS = P (dP - Delta),            (6.3, 6.4)
+//   dK = scale dS^T Q,  dQ = scale dS K
+// in three kernels, as the page divides the work: a preprocess pass for
+// Delta, a pass with K/V resident that accumulates dK and dV over all query
+// blocks, and a pass with Q resident that accumulates dQ over all key
+// blocks (the page's two stages; a block's dQ needs every key, its dK/dV
+// every query, so neither pass can produce the other's result).  With
+// natural-exp logits the page's base-2 factor ln 2 does not appear.
+//
+// gfx950 mapping:
+//  * every product is v_mfma_f32_32x32x16_bf16 on bf16 operands with fp32
+//    accumulation; P and dS are rounded to bf16 for their second product;
+//  * the resident operands (K and V fragments, or Q and dO fragments) stay
+//    in registers as MFMA B operands for the whole loop;
+//  * streamed tiles (Q and dO, or K and V) are copied HBM -> LDS with
+//    global_load_lds (no registers), rows in natural order, the 16-byte
+//    chunks of row r XOR-swizzled by a rotation f(r) of its low bits; the
+//    same tile serves row fragments (ds_read_b128, contraction over d) and
+//    transposed fragments (two ds_read_b64_tr_b16, contraction over rows),
+//    both free of bank conflicts;
+//  * the first product of a block leaves each lane one column of a 32x32
+//    accumulator (a key in the dK/dV pass, a query in the dQ pass); element
+//    i of lane half h is row 8 (i/4) + 4 h + i % 4.  Converted to bf16 it
+//    is directly the B operand of the second product, whose A operand reads
+//    tile rows in that same order (16 t + 8 w + 4 h + 0..3 for step t).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline bf16x8 cvt8(const float* x) {
+    f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+    return __builtin_convertvector(v, bf16x8);
+}
+__device__ inline void store4_bf16(uint16_t* dst, f32x4 v) {
+    *reinterpret_cast<bf16x4*>(dst) = __builtin_convertvector(v, bf16x4);
+}
+__device__ inline float bf16_to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Wait for this wave's copies (vmcnt(0)) and LDS reads, then barrier; the
+// empty asm statements keep the compiler from moving memory accesses
+// across it (a workgroup-scope fence would add nothing the waits miss).
+__device__ inline void sync_tiles() {
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) expcnt(7) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---- streamed tile geometry ----------------------------------------------
+template <int D, int ROWS, int NW> struct Tile {
+    static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+    static constexpr int ELEMS = ROWS * D;
+    static constexpr int NBLK = ROWS * CPR / 64;       // 1 KB copy blocks
+    static constexpr int BPW = NBLK / NW;              // blocks per wave
+    static_assert(BPW * NW == NBLK && BPW >= 1, "tile / waves");
+    static_assert(ROWS % 32 == 0, "tile rows");
+    // chunk swizzle: a rotation of the row's low bits (d >= 128: bits 0-3,
+    // d = 64: bits 1-3, where two rows share one 256-byte bank line)
+    __device__ static inline int f(int r) {
+        return CPR >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                         : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+};
+
+// Per-lane parts of a tile's addresses (element offsets inside the tile).
+template <int D, int ROWS, int NW> struct TileLane {
+    using T = Tile<D, ROWS, NW>;
+    static constexpr int NS = D / 16, NDB = D / 32;
+    static constexpr int NTL = NDB < 4 ? NDB : 4;
+    int cp_ofs[T::BPW];   // copy: global element offset of this lane's chunk
+    int cp_row[T::BPW];   // copy: its tile row
+    int rfo[NS];          // row fragment of step s (add blk * 32 * D)
+    int tlane[2][NTL];    // transposed fragment, read w, d-block db & 3
+
+    __device__ void init(int wave, int lane) {
+        const int col = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < T::BPW; ++i) {
+            const int p = (wave + NW * i) * 64 + lane;
+            const int row = p / T::CPR;
+            cp_row[i] = row;
+            cp_ofs[i] = row * D + ((p % T::CPR) ^ T::f(row)) * 8;
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) rfo[s] = col * D + (((2 * s + h) ^ T::f(col)) * 8);
+        const int g16 = lane >> 4, rr = lane & 15;
+        const int vh = g16 >> 1, vdh = g16 & 1, vi = rr >> 2, vq = rr & 3;
+        const int lrow = 4 * vh + vi;          // row inside the 8-row group
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+            for (int x = 0; x < NTL; ++x) {
+                const int lc = 4 * x + 2 * vdh + (vq >> 1);
+                // f depends on the row's low 4 bits only: (8 w + lrow)
+                tlane[w][x] = lrow * D + (lc ^ T::f(8 * w + lrow)) * 8 + (vq & 1) * 4;
+            }
+    }
+    // copy tile rows [r0, r0 + ROWS) of a [n, D] matrix; rows >= n read row
+    // n - 1 (finite values the masks give weight 0)
+    __device__ void copy(const uint16_t* base, int r0, int n, uint16_t* dst, int wave) const {
+        const uint16_t* src = base + (size_t)r0 * D;
+        const int last = n - 1 - r0;
+#pragma unroll
+        for (int i = 0; i < T::BPW; ++i) {
+            const int o = cp_ofs[i] + (min(cp_row[i], last) - cp_row[i]) * D;
+            __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (wave + NW * i) * 512),
+                                             16, 0, 0);
+        }
+    }
+    __device__ bf16x8 row_frag(const uint16_t* t, int blk, int s) const {
+        return *reinterpret_cast<const bf16x8*>(t + blk * 32 * D + rfo[s]);
+    }
+    // A operand whose contraction runs over rows 16 t + 8 w + 4 h + (0..3)
+    // of 32-row block blk, for d columns 32 db + lane % 32
+    __device__ bf16x8 tr_frag(const uint16_t* tl, int blk, int t, int db) const {
+        s16x4 u[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const uint16_t* a = tl + (32 * blk + 16 * t + 8 * w) * D + (db & ~3) * 32 +
+                                tlane[w][db & (NTL - 1)];
+            u[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(FA_LDS void*)a);
+        }
+        const s16x8 v8 = __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v8);
+    }
+};
+
+// ===========================================================================
+// Preprocess: Delta_i = sum_d dO_id O_id and LSE2_i = LSE_i log2(e) (the
+// forward's natural-log LSE in the base the exponentials use).  D/8 lanes
+// per row, one 16-byte chunk each, reduced across the lanes of the row.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256)
+void fa_bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                       const float* __restrict__ LSE, float* __restrict__ delta,
+                       float* __restrict__ lse2, int rows)
+{
+    constexpr int TPR = D / 8;            // lanes per row (8 or 16)
+    const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+    const int ch = threadIdx.x % TPR;
+    float acc = 0.f;
+    if (row < rows) {
+        const u16x8 o = *reinterpret_cast<const u16x8*>(O + (size_t)row * D + ch * 8);
+        const u16x8 g = *reinterpret_cast<const u16x8*>(dO + (size_t)row * D + ch * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += bf16_to_f32(o[e]) * bf16_to_f32(g[e]);
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
+    if (row < rows && ch == 0) {
+        delta[row] = acc;
+        lse2[row] = LSE[row] * kLog2e;
+    }
+}
+
+// ===========================================================================
+// dK, dV: each wave keeps 32 keys' K and V fragments in registers and their
+// dK^T, dV^T accumulators (one wave per SIMD, so the accumulators can live
+// in AGPRs); the workgroup streams Q and dO tiles of BQ queries.  Per
+// 32-query block: S = Q K^T and dP = dO V^T (lane = key), P and dS, then
+// dV^T += dO^T P and dK^T += Q^T dS.
+// ===========================================================================
+constexpr int kKVWaves = 4;                 // waves per workgroup, 32 keys each
+constexpr int kKVKeys = 32 * kKVWaves;      // keys per workgroup
+constexpr int kKVBQ = 64;                   // queries per streamed tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kKVWaves)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                        const float* __restrict__ lse2, const float* __restrict__ delta,
+                        uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                        int BH, int Lq, int Lk, int nkb, float c, float scale)
+{
+    constexpr int NW = kKVWaves, BQ = kKVBQ, NQB = BQ / 32;
+    using L = TileLane<D, BQ, NW>;
+    constexpr int NS = L::NS, NDB = L::NDB;
+    __shared__ __attribute__((aligned(1024))) uint16_t Qb0[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qb1[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ob0[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ob1[L::T::ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, h = lane >> 5;
+
+    // key blocks of a head on one XCD; causal: the first key blocks (seen by
+    // the most queries) start first
+    int bh, kb;
+    {
+        const int p = blockIdx.x;
+        if ((BH & 7) == 0) {
+            const int own = BH >> 3, slot = p >> 3;
+            bh = (p & 7) + 8 * (slot % own);
+            kb = slot / own;
+        } else {
+            bh = p % BH;
+            kb = p / BH;
+        }
+    }
+    const int key0 = kb * kKVKeys;
+    const int kw0 = key0 + wave * 32;          // this wave's keys kw0 .. kw0 + 31
+    const int key = kw0 + col;                 // this lane's key (accumulator column)
+    const uint16_t* Qh = Q + (size_t)bh * Lq * D;
+    const uint16_t* Oh = dO + (size_t)bh * Lq * D;
+    const float* lse2h = lse2 + (size_t)bh * Lq;
+    const float* delh = delta + (size_t)bh * Lq;
+
+    // resident B operands: K^T and V^T fragments (lane = key, 8 d values)
+    bf16x8 kf[NS], vf[NS];
+    {
+        const uint16_t* Kr = K + ((size_t)bh * Lk + key) * D;
+        const uint16_t* Vr = V + ((size_t)bh * Lk + key) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kf[s] = key < Lk ? *reinterpret_cast<const bf16x8*>(Kr + 16 * s + 8 * h) : bf16x8{};
+            vf[s] = key < Lk ? *reinterpret_cast<const bf16x8*>(Vr + 16 * s + 8 * h) : bf16x8{};
+        }
+    }
+    f32x16 dkt[NDB], dvt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
+
+    L ln;
+    ln.init(wave, lane);
+    // query tiles that can see a key of this block: causal, q >= key0
+    const int jt0 = CAUSAL ? key0 / BQ : 0;
+    const int jt1 = (Lq + BQ - 1) / BQ;
+
+    auto step = [&](int jt, const uint16_t* Qc, const uint16_t* Oc, uint16_t* Qn, uint16_t* On) {
+        if (jt + 1 < jt1) {
+            ln.copy(Qh, (jt + 1) * BQ, Lq, Qn, wave);
+            ln.copy(Oh, (jt + 1) * BQ, Lq, On, wave);
+        }
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int q0 = jt * BQ + 32 * qb;
+            // the block's queries all precede this wave's keys, or lie past Lq
+            if ((CAUSAL && q0 + 31 < kw0) || q0 >= Lq) continue;
+            f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                s_acc = mfma(ln.row_frag(Qc, qb, s), kf[s], s_acc);
+                dp_acc = mfma(ln.row_frag(Oc, qb, s), vf[s], dp_acc);
+            }
+            // element i: query q0 + 8 (i/4) + 4 h + i % 4 (4 runs of 4)
+            // (scalar loads: bh * Lq need not keep 4-float runs 16-byte aligned)
+            float lq[16], dq[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qq = min(q0 + 8 * (i / 4) + 4 * h + (i % 4), Lq - 1);
+                lq[i] = lse2h[qq];
+                dq[i] = delh[qq];
+            }
+            const bool edge = (q0 + 31 >= Lq) || (key0 + kKVKeys > Lk) || (CAUSAL && q0 < kw0 + 31);
+            float p[16], ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qi = q0 + 8 * (i / 4) + 4 * h + (i % 4);
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq[i]));
+                if (edge && (qi >= Lq || key >= Lk || (CAUSAL && key > qi))) pv = 0.f;
+                p[i] = pv;
+                ds[i] = pv * (dp_acc[i] - dq[i]);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 pf = cvt8(p + 8 * t);
+                const bf16x8 sf = cvt8(ds + 8 * t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvt[db] = mfma(ln.tr_frag(Oc, qb, t, db), pf, dvt[db]);
+                    dkt[db] = mfma(ln.tr_frag(Qc, qb, t, db), sf, dkt[db]);
+                }
+            }
+        }
+        sync_tiles();
+    };
+    if (jt0 < jt1) {
+        ln.copy(Qh, jt0 * BQ, Lq, Qb0, wave);
+        ln.copy(Oh, jt0 * BQ, Lq, Ob0, wave);
+        sync_tiles();
+        for (int jt = jt0; jt < jt1; jt += 2) {
+            step(jt, Qb0, Ob0, Qb1, Ob1);
+            if (jt + 1 < jt1) step(jt + 1, Qb1, Ob1, Qb0, Ob0);
+        }
+    }
+    // dK = scale dS^T Q, dV = P^T dO; lane = key, rows = d
+    if (key < Lk) {
+        uint16_t* dKr = dK + ((size_t)bh * Lk + key) * D;
+        uint16_t* dVr = dV + ((size_t)bh * Lk + key) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dc = db * 32 + 8 * g + 4 * h;
+                f32x4 k4 = {dkt[db][4 * g], dkt[db][4 * g + 1], dkt[db][4 * g + 2], dkt[db][4 * g + 3]};
+                f32x4 v4 = {dvt[db][4 * g], dvt[db][4 * g + 1], dvt[db][4 * g + 2], dvt[db][4 * g + 3]};
+                store4_bf16(dKr + dc, k4 * scale);
+                store4_bf16(dVr + dc, v4);
+            }
+    }
+}
+
+// ===========================================================================
+// dQ: each wave keeps 32 queries' Q and dO fragments in registers and their
+// dQ^T accumulator; the workgroup streams K and V tiles of BK keys, as in
+// the forward.  Per 32-key block: S^T = K Q^T and dP^T = V dO^T (lane =
+// query), P^T and dS^T, then dQ^T += K^T dS^T.
+// ===========================================================================
+constexpr int kQWaves = 8;                  // waves per workgroup, 32 queries each
+constexpr int kQRows = 32 * kQWaves;        // queries per workgroup
+constexpr int kQBK = 64;                    // keys per streamed tile
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kQWaves)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                      const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                      const float* __restrict__ lse2, const float* __restrict__ delta,
+                      uint16_t* __restrict__ dQ, int BH, int Lq, int Lk, int nqb, float c,
+                      float scale)
+{
+    constexpr int NW = kQWaves, BK = kQBK, NKB = BK / 32;
+    using L = TileLane<D, BK, NW>;
+    constexpr int NS = L::NS, NDB = L::NDB;
+    __shared__ __attribute__((aligned(1024))) uint16_t Kb0[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Kb1[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vb0[L::T::ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vb1[L::T::ELEMS];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, h = lane >> 5;
+
+    int bh, lvl;
+    {
+        const int p = blockIdx.x;
+        if ((BH & 7) == 0) {
+            const int own = BH >> 3, slot = p >> 3;
+            bh = (p & 7) + 8 * (slot % own);
+            lvl = slot / own;
+        } else {
+            bh = p % BH;
+            lvl = p / BH;
+        }
+    }
+    const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
+    const int q0 = qb * kQRows;
+    const int q0w = q0 + wave * 32;
+    const int qi = q0w + col;                  // this lane's query (accumulator column)
+    const uint16_t* Kh = K + (size_t)bh * Lk * D;
+    const uint16_t* Vh = V + (size_t)bh * Lk * D;
+
+    bf16x8 qf[NS], of[NS];
+    {
+        const uint16_t* Qr = Q + ((size_t)bh * Lq + qi) * D;
+        const uint16_t* Or = dO + ((size_t)bh * Lq + qi) * D;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            qf[s] = qi < Lq ? *reinterpret_cast<const bf16x8*>(Qr + 16 * s + 8 * h) : bf16x8{};
+            of[s] = qi < Lq ? *reinterpret_cast<const bf16x8*>(Or + 16 * s + 8 * h) : bf16x8{};
+        }
+    }
+    const float lq = qi < Lq ? lse2[(size_t)bh * Lq + qi] : 0.f;
+    const float dq = qi < Lq ? delta[(size_t)bh * Lq + qi] : 0.f;
+    f32x16 dqt[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
+
+    L ln;
+    ln.init(wave, lane);
+    const int kv_end = CAUSAL ? min(Lk, q0 + kQRows) : Lk;
+    const int nt = (kv_end + BK - 1) / BK;
+
+    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
+        if (j + 1 < nt) {
+            ln.copy(Kh, (j + 1) * BK, Lk, Kn, wave);
+            ln.copy(Vh, (j + 1) * BK, Lk, Vn, wave);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int k0 = j * BK + 32 * kb;
+            if ((CAUSAL && k0 > q0w + 31) || k0 >= Lk) continue;
+            f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                s_acc = mfma(ln.row_frag(Kc, kb, s), qf[s], s_acc);
+                dp_acc = mfma(ln.row_frag(Vc, kb, s), of[s], dp_acc);
+            }
+            const bool edge = (k0 + 31 >= Lk) || (qi >= Lq) || (CAUSAL && k0 + 31 > q0w);
+            float ds[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kj = k0 + 8 * (i / 4) + 4 * h + (i % 4);   // element i: key
+                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq));
+                if (edge && (kj >= Lk || qi >= Lq || (CAUSAL && kj > qi))) pv = 0.f;
+                ds[i] = pv * (dp_acc[i] - dq);
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const bf16x8 sf = cvt8(ds + 8 * t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) dqt[db] = mfma(ln.tr_frag(Kc, kb, t, db), sf, dqt[db]);
+            }
+        }
+        sync_tiles();
+    };
+    ln.copy(Kh, 0, Lk, Kb0, wave);
+    ln.copy(Vh, 0, Lk, Vb0, wave);
+    sync_tiles();
+    for (int j = 0; j < nt; j += 2) {
+        step(j, Kb0, Vb0, Kb1, Vb1);
+        if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+    }
+    // dQ = scale dS K; lane = query, rows = d
+    if (qi < Lq) {
+        uint16_t* dQr = dQ + ((size_t)bh * Lq + qi) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 v4 = {dqt[db][4 * g], dqt[db][4 * g + 1], dqt[db][4 * g + 2], dqt[db][4 * g + 3]};
+                store4_bf16(dQr + db * 32 + 8 * g + 4 * h, v4 * scale);
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int H, int Lq, int Lk, float scale, float* delta, float* lse2,
+                        hipStream_t stream)
+{
+    const int BH = B * H;
+    const int rows = BH * Lq;
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, stream, static_cast<const uint16_t*>(o),
+                       static_cast<const uint16_t*>(dout), lse, delta, lse2, rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const float c = scale * kLog2e;
+    const int nkb = (Lk + kKVKeys - 1) / kKVKeys;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BH)),
+                       dim3(64 * kKVWaves), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(dout), lse2, delta,
+                       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, Lq, Lk, nkb,
+                       c, scale);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int nqb = (Lq + kQRows - 1) / kQRows;
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)),
+                       dim3(64 * kQWaves), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(dout), lse2, delta,
+                       static_cast<uint16_t*>(dq), BH, Lq, Lk, nqb, c, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int d) { return d == 64 || d == 128; }
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      int B, int H, int Lq, int Lk, int d, bool causal, float scale,
+                      float* delta, float* lse2, hipStream_t stream)
+{
+    switch (d) {
+    case 64:
+        return causal ? launch_bwd_d<64, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream)
+                      : launch_bwd_d<64, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream);
+    case 128:
+        return causal ? launch_bwd_d<128, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream)
+                      : launch_bwd_d<128, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

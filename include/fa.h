@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3   /* 2: fa_fwd_window; 3: fa_fwd_splitkv */
+#define FA_ABI_VERSION 4   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd */
 
 enum fa_status {
     FA_OK = 0,
@@ -136,6 +136,36 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /* Workspace bytes fa_fwd_splitkv needs, or 0 for invalid arguments
  * (B, H, Lq < 1, d not 64/128/256, num_splits outside 1 .. 64).  Host-only. */
 size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits);
+
+/*
+ * bf16 backward: the gradients dq, dk, dv of sum(dout * o) for the forward
+ * o = fa_fwd(q, k, v, causal, scale), following "第 08 章: Flash Attention——
+ * 分块注意力" (chuoer47.github.io), section 6 "反向":
+ *     Delta_i = sum_t dout[i,t] o[i,t]
+ *     P_ij    = exp(scale q_i.k_j - lse_i)      (recomputed, j in A_i)
+ *     dv = P^T dout,   dP = dout v^T,   dS = P (dP - Delta),
+ *     dq = scale dS k,  dk = scale dS^T q
+ * o and lse must be the outputs of fa_fwd for the same q, k, v, causal and
+ * scale (lse is the natural-log LSE fa_fwd writes).  Products run on bf16
+ * MFMA with fp32 accumulation (P and dS rounded to bf16 for their second
+ * product); dq, dk, dv are written in bf16, round to nearest even.
+ *   layout    : q, o, dout, dq [B, H, Lq, d]; k, v, dk, dv [B, H, Lk, d];
+ *               lse [B, H, Lq] fp32; dense row-major, 16-byte aligned
+ *   d         : 64 or 128 (other values: FA_ERR_UNSUPPORTED_D)
+ *   workspace : device memory of at least fa_bwd_workspace_size(B, H, Lq)
+ *               bytes, 16-byte aligned, caller-owned scratch (holds Delta);
+ *               concurrent calls need separate workspaces
+ * Three kernels are enqueued on `stream`.  dq, dk, dv and the workspace must
+ * not overlap any other argument or each other.  Errors as fa_fwd, plus
+ * FA_ERR_WORKSPACE for a small workspace.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int Lq, int Lk,
+           int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
+/* Workspace bytes fa_bwd needs (0 for B, H or Lq < 1).  Host-only. */
+size_t fa_bwd_workspace_size(int B, int H, int Lq);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

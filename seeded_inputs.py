@@ -124,6 +124,14 @@ def make_inputs(seed: int, B: int, H: int, Lq: int, Lk: int, d: int,
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def make_grad(seed: int, B: int, H: int, Lq: int, d: int) -> np.ndarray:
+    """Upstream gradient dO [B,H,Lq,d] for the backward pass: standard
+    normal (the pages' benchmark draws it with randn_like), from its own
+    generator (seed + 1000), rounded to bfloat16 bits."""
+    rng = np.random.default_rng(seed + 1000)
+    return round_to_bf16_bits(rng.standard_normal((B, H, Lq, d), dtype=np.float32))
+
+
 def widen(x: np.ndarray) -> np.ndarray:
     """Storage array (bf16 bits or fp32) -> exact float64 values."""
     if x.dtype == np.uint16:

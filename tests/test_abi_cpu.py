@@ -155,3 +155,37 @@ def test_splitkv_validation_errors():
     assert _st_split(workspace_bytes=need - 1) == 8
     assert _st_split(workspace=Q + 256) == 6         # overlaps q
     assert _st_split(d=32) == 3
+
+
+DO, DQ, DK, DV, WB = (0x10000000 * i for i in range(8, 13))
+
+
+def _st_bwd(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, B=1, H=2,
+                Lq=128, Lk=128, d=64, causal=1, scale=0.125, workspace=WB,
+                workspace_bytes=1 << 20)
+    args.update(kw)
+    try:
+        fa.fa_bwd(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+def test_bwd_workspace_size():
+    assert fa.bwd_workspace_size(1, 2, 128) == 2 * ((2 * 128 * 4 + 255) // 256 * 256)
+    assert fa.bwd_workspace_size(2, 3, 77) == 2 * ((6 * 77 * 4 + 255) // 256 * 256)
+    assert fa.bwd_workspace_size(0, 2, 128) == 0
+
+
+def test_bwd_validation_errors():
+    assert _st_bwd(dout=0) == 1
+    assert _st_bwd(workspace=0) == 1
+    assert _st_bwd(Lk=0) == 2
+    assert _st_bwd(d=256) == 3 and _st_bwd(d=96) == 3
+    assert _st_bwd(dq=DQ + 8) == 4
+    assert _st_bwd(scale=0.0) == 5
+    assert _st_bwd(causal=2) == 6
+    assert _st_bwd(workspace_bytes=fa.bwd_workspace_size(1, 2, 128) - 1) == 8
+    assert _st_bwd(dk=Q + 64) == 6         # an output overlapping an input
+    assert _st_bwd(dv=DK + 16) == 6        # two outputs overlapping
