@@ -211,6 +211,10 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     __shared__ __attribute__((aligned(1024))) uint16_t Qb1[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Ob0[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Ob1[L::T::ELEMS];
+    // the tile's LSE2 and Delta values, copied with it (4 bytes per lane)
+    static_assert(BQ == 64, "one 64-lane copy per vector");
+    __shared__ __attribute__((aligned(256))) float Sb0[2 * BQ];
+    __shared__ __attribute__((aligned(256))) float Sb1[2 * BQ];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, h = lane >> 5;
@@ -258,10 +262,19 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int jt0 = CAUSAL ? key0 / BQ : 0;
     const int jt1 = (Lq + BQ - 1) / BQ;
 
-    auto step = [&](int jt, const uint16_t* Qc, const uint16_t* Oc, uint16_t* Qn, uint16_t* On) {
+    // wave 0 copies the tile's LSE2 values, wave 1 its Delta values
+    auto copy_stats = [&](int jt, float* Sd) {
+        if (wave < 2) {
+            const float* src = (wave == 0 ? lse2h : delh) + min(jt * BQ + lane, Lq - 1);
+            __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(Sd + wave * BQ), 4, 0, 0);
+        }
+    };
+    auto step = [&](int jt, const uint16_t* Qc, const uint16_t* Oc, const float* Sc,
+                    uint16_t* Qn, uint16_t* On, float* Sn) {
         if (jt + 1 < jt1) {
             ln.copy(Qh, (jt + 1) * BQ, Lq, Qn, wave);
             ln.copy(Oh, (jt + 1) * BQ, Lq, On, wave);
+            copy_stats(jt + 1, Sn);
         }
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -274,14 +287,16 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                 s_acc = mfma(ln.row_frag(Qc, qb, s), kf[s], s_acc);
                 dp_acc = mfma(ln.row_frag(Oc, qb, s), vf[s], dp_acc);
             }
-            // element i: query q0 + 8 (i/4) + 4 h + i % 4 (4 runs of 4)
-            // (scalar loads: bh * Lq need not keep 4-float runs 16-byte aligned)
+            // element i: query q0 + 8 (i/4) + 4 h + i % 4, four runs of four
+            // consecutive values in the tile's LSE2 / Delta copies
             float lq[16], dq[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qq = min(q0 + 8 * (i / 4) + 4 * h + (i % 4), Lq - 1);
-                lq[i] = lse2h[qq];
-                dq[i] = delh[qq];
+            for (int g = 0; g < 4; ++g) {
+                const int r = 32 * qb + 8 * g + 4 * h;
+                const f32x4 a = *reinterpret_cast<const f32x4*>(Sc + r);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(Sc + BQ + r);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { lq[4 * g + e] = a[e]; dq[4 * g + e] = b[e]; }
             }
             const bool edge = (q0 + 31 >= Lq) || (key0 + kKVKeys > Lk) || (CAUSAL && q0 < kw0 + 31);
             float p[16], ds[16];
@@ -309,10 +324,11 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     if (jt0 < jt1) {
         ln.copy(Qh, jt0 * BQ, Lq, Qb0, wave);
         ln.copy(Oh, jt0 * BQ, Lq, Ob0, wave);
+        copy_stats(jt0, Sb0);
         sync_tiles();
         for (int jt = jt0; jt < jt1; jt += 2) {
-            step(jt, Qb0, Ob0, Qb1, Ob1);
-            if (jt + 1 < jt1) step(jt + 1, Qb1, Ob1, Qb0, Ob0);
+            step(jt, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
+            if (jt + 1 < jt1) step(jt + 1, Qb1, Ob1, Sb1, Qb0, Ob0, Sb0);
         }
     }
     // dK = scale dS^T Q, dV = P^T dO; lane = key, rows = d
