@@ -33,6 +33,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA / fp32
 DEFAULT_WORKLOAD = "bf16_causal_16k_d128"
 KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                              "fa_fwd_kernel.hip")
+BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
+                                 "fa_bwd_kernel.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -40,25 +42,30 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel source with comments and whitespace removed, so
-    that counters stay attached to the code they were taken on and survive
-    edits that cannot change it."""
-    text = open(KERNEL_SOURCE).read()
+def kernel_source_hash(path: str = None) -> str:
+    """Hash of a kernel source (default: the forward's) with comments and
+    whitespace removed, so that counters stay attached to the code they
+    were taken on and survive edits that cannot change it."""
+    text = open(path or KERNEL_SOURCE).read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = re.sub(r"\s+", "", text)
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary for
-    this workload, or None if absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"fa_fwd_{workload}_hbm_counters.txt")
+def traffic_from_profiles(workload: str, backward: bool = False):
+    """HBM bytes per call from the committed rocprofv3 counter summary for
+    this workload and pass, or None if absent or taken on a different
+    kernel source."""
+    path = os.path.join(PROFILES, f"fa_{'bwd' if backward else 'fwd'}_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if backward:
+        h2 = re.search(r"bwd_kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+        if not h2 or h2.group(1) != kernel_source_hash(BWD_KERNEL_SOURCE):
+            return None
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
@@ -344,7 +351,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 5),
-                     "traffic": traffic_from_profiles(w.name),
+                     "traffic": traffic_from_profiles(w.name, backward),
                      "kernel_ms": round(ms_kernel, 5),
                      "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None if cpu is None else {
