@@ -216,7 +216,10 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     __shared__ __attribute__((aligned(256))) float Sb0[2 * BQ];
     __shared__ __attribute__((aligned(256))) float Sb1[2 * BQ];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: keeping it in a scalar register makes every
+    // per-wave condition below a scalar branch
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, h = lane >> 5;
 
     // key blocks of a head on one XCD; causal: the first key blocks (seen by
@@ -298,16 +301,25 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 #pragma unroll
                 for (int e = 0; e < 4; ++e) { lq[4 * g + e] = a[e]; dq[4 * g + e] = b[e]; }
             }
-            const bool edge = (q0 + 31 >= Lq) || (key0 + kKVKeys > Lk) || (CAUSAL && q0 < kw0 + 31);
             float p[16], ds[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qi = q0 + 8 * (i / 4) + 4 * h + (i % 4);
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq[i]));
-                if (edge && (qi >= Lq || key >= Lk || (CAUSAL && key > qi))) pv = 0.f;
-                p[i] = pv;
-                ds[i] = pv * (dp_acc[i] - dq[i]);
+            for (int i = 0; i < 16; ++i)
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq[i]));
+            // Masks, on the blocks that need them (a wave-uniform test).  A key
+            // past Lk needs none: its lane's column of dK, dV is never stored
+            // and no product mixes columns.  Element i holds query q0 + off + 4h
+            // with off = 8 (i/4) + i%4; it is visible iff lo <= off < hi.
+            if ((q0 + 31 >= Lq) || (CAUSAL && q0 < kw0 + 31)) {
+                const int lo = CAUSAL ? key - q0 - 4 * h : 0;   // query >= key
+                const int hi = Lq - q0 - 4 * h;                  // query < Lq
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i / 4) + (i % 4);
+                    p[i] = (off < lo || off >= hi) ? 0.f : p[i];
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp_acc[i] - dq[i]);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const bf16x8 pf = cvt8(p + 8 * t);
@@ -375,7 +387,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     __shared__ __attribute__((aligned(1024))) uint16_t Vb0[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Vb1[L::T::ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, h = lane >> 5;
 
     int bh, lvl;
@@ -433,15 +446,24 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                 s_acc = mfma(ln.row_frag(Kc, kb, s), qf[s], s_acc);
                 dp_acc = mfma(ln.row_frag(Vc, kb, s), of[s], dp_acc);
             }
-            const bool edge = (k0 + 31 >= Lk) || (qi >= Lq) || (CAUSAL && k0 + 31 > q0w);
-            float ds[16];
+            float p[16], ds[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kj = k0 + 8 * (i / 4) + 4 * h + (i % 4);   // element i: key
-                float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq));
-                if (edge && (kj >= Lk || qi >= Lq || (CAUSAL && kj > qi))) pv = 0.f;
-                ds[i] = pv * (dp_acc[i] - dq);
+            for (int i = 0; i < 16; ++i)
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq));
+            // Masks, on the blocks that need them (a wave-uniform test).  A
+            // query past Lq needs none: its lane's column of dQ is never
+            // stored.  Element i holds key k0 + off + 4h with off = 8 (i/4) +
+            // i%4; it is visible iff off < hi.
+            if ((k0 + 31 >= Lk) || (CAUSAL && k0 + 31 > q0w)) {
+                const int hi = CAUSAL ? min(Lk, qi + 1) - k0 - 4 * h : Lk - k0 - 4 * h;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int off = 8 * (i / 4) + (i % 4);
+                    p[i] = off < hi ? p[i] : 0.f;
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp_acc[i] - dq);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const bf16x8 sf = cvt8(ds + 8 * t);
