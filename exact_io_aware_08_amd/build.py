@@ -36,27 +36,48 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build)")
 
 
-def build(isa_dir: str | None = None, verbose: bool = False) -> str:
-    """Compile every source into LIB_PATH; return the path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-shared", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}",
-           f"-I{CSRC}", *DEVICE_FLAGS]
+# Per-file device flags.  The backward kernels keep their MFMA accumulators
+# in the VGPR form of the instructions (the register allocator then puts the
+# long-lived dK/dV accumulators in AGPRs without copying them back and forth
+# every loop trip); the forward kernels are faster with the default.
+FILE_FLAGS = {"fa_bwd_kernel.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def build(isa_dir: str | None = None, verbose: bool = False, csrc: str = CSRC,
+          out: str = LIB_PATH, extra_flags=()) -> str:
+    """Compile every source (one object each, in parallel) and link them
+    into ``out``; return the path."""
+    import tempfile
+    base = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{csrc}",
+            *DEVICE_FLAGS, *extra_flags]
     if isa_dir:
         os.makedirs(isa_dir, exist_ok=True)
-        cmd += ["-save-temps"]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, cwd=isa_dir or PKG, capture_output=True, text=True)
+        base += ["-save-temps"]
     noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+
+    def run(cmds, cwd):
+        procs = [(c, subprocess.Popen(c, cwd=cwd, stdout=subprocess.PIPE,
+                                      stderr=subprocess.PIPE, text=True)) for c in cmds]
+        for c, pr in procs:
+            _, stderr = pr.communicate()
+            err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+            if verbose:
+                print(" ".join(c), flush=True)
+            if pr.returncode != 0:
+                raise RuntimeError(f"hipcc failed ({pr.returncode}):\n{err}")
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+
+    with tempfile.TemporaryDirectory() as tmpdir:
+        objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        run([base + FILE_FLAGS.get(s, []) + ["-c", os.path.join(csrc, s), "-o", o]
+             for s, o in zip(SOURCES, objs)], isa_dir or tmpdir)
+        tmp = out + ".tmp"
+        run([[hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]],
+            tmpdir)
+        os.replace(tmp, out)
+    return out
 
 
 def main(argv=None):

@@ -130,7 +130,7 @@ int window_mask(int left, int right, int Lq, int Lk, MaskSpec* m) {
     return FA_OK;
 }
 
-// Workspace of fa_bwd: Delta then LSE * log2(e), [B*H][Lq] fp32 each.
+// Workspace of fa_bwd: -Delta then -LSE / scale, [B*H][Lq] fp32 each.
 std::size_t bwd_workspace_bytes(long long bh, int Lq) {
     return 2 * round256((std::size_t)bh * Lq * sizeof(float));
 }
@@ -225,10 +225,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
         for (int j = i + 1; j < 4; ++j)
             if (overlaps(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return FA_ERR_ARG;
     }
-    float* delta = static_cast<float*>(workspace);
-    float* lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + wbytes / 2);
+    float* ndelta = static_cast<float*>(workspace);
+    float* nlse = reinterpret_cast<float*>(static_cast<char*>(workspace) + wbytes / 2);
     const hipError_t err = fa::launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d,
-                                          causal == 1, scale, delta, lse2, stream);
+                                          causal == 1, scale, ndelta, nlse, stream);
     return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -156,15 +156,17 @@ template <int D, int ROWS, int NW> struct TileLane {
 };
 
 // ===========================================================================
-// Preprocess: Delta_i = sum_d dO_id O_id and LSE2_i = LSE_i log2(e) (the
-// forward's natural-log LSE in the base the exponentials use).  D/8 lanes
-// per row, one 16-byte chunk each, reduced across the lanes of the row.
+// Preprocess: per query row, -Delta_i = -sum_d dO_id O_id and -LSE_i / scale,
+// the starting values of the dP and S accumulators (so that the products
+// give dP - Delta and S - LSE / scale directly, and P = exp2(c (S - LSE /
+// scale)) with c = scale log2(e)).  D/8 lanes per row, one 16-byte chunk
+// each, reduced across the lanes of the row.
 // ===========================================================================
 template <int D>
 __global__ __launch_bounds__(256)
 void fa_bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                       const float* __restrict__ LSE, float* __restrict__ delta,
-                       float* __restrict__ lse2, int rows)
+                       const float* __restrict__ LSE, float* __restrict__ ndelta,
+                       float* __restrict__ nlse, int rows, float scale)
 {
     constexpr int TPR = D / 8;            // lanes per row (8 or 16)
     const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
@@ -179,8 +181,8 @@ void fa_bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restric
 #pragma unroll
     for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, TPR);
     if (row < rows && ch == 0) {
-        delta[row] = acc;
-        lse2[row] = LSE[row] * kLog2e;
+        ndelta[row] = -acc;
+        nlse[row] = -LSE[row] / scale;
     }
 }
 
@@ -190,6 +192,15 @@ void fa_bwd_pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restric
 // in AGPRs); the workgroup streams Q and dO tiles of BQ queries.  Per
 // 32-query block: S = Q K^T and dP = dO V^T (lane = key), P and dS, then
 // dV^T += dO^T P and dK^T += Q^T dS.
+//
+// With one wave per SIMD nothing else hides a wave's LDS latency, so each
+// block is software-pipelined: its S and dP products run on row fragments
+// read during the previous block's products, while its transposed fragments
+// and statistics are read; its dV and dK products run while the next
+// block's row fragments are read.  The next tile's row fragments are read
+// before its first block, so the tile barrier sits just before the second
+// block's dV/dK products, and the copy it guards goes into the tile just
+// finished (two buffers suffice).
 // ===========================================================================
 constexpr int kKVWaves = 4;                 // waves per workgroup, 32 keys each
 constexpr int kKVKeys = 32 * kKVWaves;      // keys per workgroup
@@ -200,19 +211,20 @@ __global__ __launch_bounds__(64 * kKVWaves)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                        const float* __restrict__ lse2, const float* __restrict__ delta,
+                        const float* __restrict__ nlse, const float* __restrict__ ndelta,
                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                         int BH, int Lq, int Lk, int nkb, float c, float scale)
 {
-    constexpr int NW = kKVWaves, BQ = kKVBQ, NQB = BQ / 32;
+    constexpr int NW = kKVWaves, BQ = kKVBQ;
     using L = TileLane<D, BQ, NW>;
     constexpr int NS = L::NS, NDB = L::NDB;
     __shared__ __attribute__((aligned(1024))) uint16_t Qb0[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Qb1[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Ob0[L::T::ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Ob1[L::T::ELEMS];
-    // the tile's LSE2 and Delta values, copied with it (4 bytes per lane)
-    static_assert(BQ == 64, "one 64-lane copy per vector");
+    // the tile's -LSE / scale and -Delta values, copied with it (4 bytes per
+    // lane)
+    static_assert(BQ == 64, "one 64-lane copy per vector, two 32-query blocks per tile");
     __shared__ __attribute__((aligned(256))) float Sb0[2 * BQ];
     __shared__ __attribute__((aligned(256))) float Sb1[2 * BQ];
 
@@ -241,8 +253,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     const int key = kw0 + col;                 // this lane's key (accumulator column)
     const uint16_t* Qh = Q + (size_t)bh * Lq * D;
     const uint16_t* Oh = dO + (size_t)bh * Lq * D;
-    const float* lse2h = lse2 + (size_t)bh * Lq;
-    const float* delh = delta + (size_t)bh * Lq;
+    const float* nlseh = nlse + (size_t)bh * Lq;
+    const float* ndelh = ndelta + (size_t)bh * Lq;
 
     // resident B operands: K^T and V^T fragments (lane = key, 8 d values)
     bf16x8 kf[NS], vf[NS];
@@ -261,86 +273,155 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
     L ln;
     ln.init(wave, lane);
-    // query tiles that can see a key of this block: causal, q >= key0
+    // query tiles that can see a key of this block: causal, q >= key0.  Every
+    // wave runs every block of these tiles (a block wholly before a wave's
+    // keys, or past Lq, is masked to zero), so the waves stay in step.
     const int jt0 = CAUSAL ? key0 / BQ : 0;
     const int jt1 = (Lq + BQ - 1) / BQ;
 
-    // wave 0 copies the tile's LSE2 values, wave 1 its Delta values
-    auto copy_stats = [&](int jt, float* Sd) {
+    // copy query tile jt (Q, dO rows and their statistics); wave 0 copies
+    // the -LSE / scale values, wave 1 the -Delta values
+    auto copy_tile = [&](int jt, uint16_t* Qd, uint16_t* Od, float* Sd) {
+        ln.copy(Qh, jt * BQ, Lq, Qd, wave);
+        ln.copy(Oh, jt * BQ, Lq, Od, wave);
         if (wave < 2) {
-            const float* src = (wave == 0 ? lse2h : delh) + min(jt * BQ + lane, Lq - 1);
+            const float* src = (wave == 0 ? nlseh : ndelh) + min(jt * BQ + lane, Lq - 1);
             __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(Sd + wave * BQ), 4, 0, 0);
         }
     };
-    auto step = [&](int jt, const uint16_t* Qc, const uint16_t* Oc, const float* Sc,
-                    uint16_t* Qn, uint16_t* On, float* Sn) {
-        if (jt + 1 < jt1) {
-            ln.copy(Qh, (jt + 1) * BQ, Lq, Qn, wave);
-            ln.copy(Oh, (jt + 1) * BQ, Lq, On, wave);
-            copy_stats(jt + 1, Sn);
+
+    // carried from one block to the next: the next block's Q row fragments
+    // (contraction over d) and the start of its S accumulator (-LSE / scale
+    // of its queries: element i is query 8 (i/4) + 4 h + i % 4 of the block,
+    // four runs of four consecutive values in the tile's statistics)
+    bf16x8 rq[NS];
+    f32x16 s_init;
+    auto read_stats = [&](const float* St, int qb, f32x16& dst) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(St + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[4 * g + e] = a[e];
         }
+    };
+
+    // Block qb (0 or 1) of tile jt, held in (Qc, Oc, Sc); (Qn, On, Sn) hold
+    // the next tile.  Each product below is one step followed by a
+    // scheduling fence, with the reads (and exponentials) issued beside it
+    // placed by hand.  Block 1 ends the tile: halfway through its dV/dK
+    // products it waits at the barrier (tile jt + 1 has landed and every
+    // wave is done with tile jt) and starts the copy of tile jt + 2 into
+    // (Qc, Oc, Sc).
+    auto block = [&](int jt, auto qbc, uint16_t* Qc, uint16_t* Oc, float* Sc,
+                     const uint16_t* Qn, const uint16_t* On, const float* Sn) {
+        constexpr int qb = decltype(qbc)::value;
+        const int q0 = jt * BQ + 32 * qb;
+        // X: S = Q K^T (from the carried fragments), then dP = dO V^T; the
+        // dO row fragments are read two steps ahead, then the t = 0 halves
+        // of the transposed fragments; the exponentials start two steps
+        // after S is complete.  s_acc = S - LSE / scale, dp_acc = dP - Delta.
+        f32x16 s_acc = s_init, dp_acc;
+        read_stats(Sc + BQ, qb, dp_acc);
+        bf16x8 ro[NS], to0[NDB], tq0[NDB];
+        ro[0] = ln.row_frag(Oc, qb, 0);
+        ro[1] = ln.row_frag(Oc, qb, 1);
+        float p[16];
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            const int q0 = jt * BQ + 32 * qb;
-            // the block's queries all precede this wave's keys, or lie past Lq
-            if ((CAUSAL && q0 + 31 < kw0) || q0 >= Lq) continue;
-            f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                s_acc = mfma(ln.row_frag(Qc, qb, s), kf[s], s_acc);
-                dp_acc = mfma(ln.row_frag(Oc, qb, s), vf[s], dp_acc);
+        for (int m = 0; m < 2 * NS; ++m) {
+            if (m < NS) s_acc = mfma(rq[m], kf[m], s_acc);
+            else dp_acc = mfma(ro[m - NS], vf[m - NS], dp_acc);
+            if (m + 2 < NS) {
+                ro[m + 2] = ln.row_frag(Oc, qb, m + 2);
+            } else if (m + 2 - NS < 2 * NDB) {
+                const int f = m + 2 - NS;
+                if (f & 1) tq0[f >> 1] = ln.tr_frag(Qc, qb, 0, f >> 1);
+                else to0[f >> 1] = ln.tr_frag(Oc, qb, 0, f >> 1);
             }
-            // element i: query q0 + 8 (i/4) + 4 h + i % 4, four runs of four
-            // consecutive values in the tile's LSE2 / Delta copies
-            float lq[16], dq[16];
+            if (m >= NS + 2) {
+                constexpr int kSteps = NS - 2;
+                const int e0 = (m - NS - 2) * 16 / kSteps, e1 = (m - NS - 1) * 16 / kSteps;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = 32 * qb + 8 * g + 4 * h;
-                const f32x4 a = *reinterpret_cast<const f32x4*>(Sc + r);
-                const f32x4 b = *reinterpret_cast<const f32x4*>(Sc + BQ + r);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) { lq[4 * g + e] = a[e]; dq[4 * g + e] = b[e]; }
+                for (int e = e0; e < e1; ++e) p[e] = __builtin_amdgcn_exp2f(s_acc[e] * c);
             }
-            float p[16], ds[16];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Masks, on the blocks that need them (a wave-uniform test).  A key
+        // past Lk needs none: its lane's column of dK, dV is never stored and
+        // no product mixes columns.  Element i holds query q0 + off + 4h with
+        // off = 8 (i/4) + i%4; it is visible iff lo <= off < hi.
+        if ((q0 + 31 >= Lq) || (CAUSAL && q0 < kw0 + 31)) {
+            const int lo = CAUSAL ? key - q0 - 4 * h : 0;   // query >= key
+            const int hi = Lq - q0 - 4 * h;                  // query < Lq
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq[i]));
-            // Masks, on the blocks that need them (a wave-uniform test).  A key
-            // past Lk needs none: its lane's column of dK, dV is never stored
-            // and no product mixes columns.  Element i holds query q0 + off + 4h
-            // with off = 8 (i/4) + i%4; it is visible iff lo <= off < hi.
-            if ((q0 + 31 >= Lq) || (CAUSAL && q0 < kw0 + 31)) {
-                const int lo = CAUSAL ? key - q0 - 4 * h : 0;   // query >= key
-                const int hi = Lq - q0 - 4 * h;                  // query < Lq
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i / 4) + (i % 4);
+                p[i] = (off < lo || off >= hi) ? 0.f : p[i];
+            }
+        }
+        float ds[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = 8 * (i / 4) + (i % 4);
-                    p[i] = (off < lo || off >= hi) ? 0.f : p[i];
+        for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp_acc[i];
+        const bf16x8 pf[2] = {cvt8(p), cvt8(p + 8)};
+        const bf16x8 sf[2] = {cvt8(ds), cvt8(ds + 8)};
+        // Y: dV^T += dO^T P, dK^T += Q^T dS, the t = 0 half then the t = 1
+        // half; the t = 1 transposed fragments are read during the first
+        // half, the next block's Q row fragments and S start during the
+        // second.
+        bf16x8 to1[NDB], tq1[NDB];
+        const uint16_t* Qx = qb == 1 ? Qn : Qc;
+        const float* Sx = qb == 1 ? Sn : Sc;
+        constexpr int kY = 4 * NDB, kHalf = 2 * NDB;
+#pragma unroll
+        for (int m = 0; m < kY; ++m) {
+            const int t = m / kHalf, db = (m % kHalf) >> 1;
+            if ((m & 1) == 0) dvt[db] = mfma(t ? to1[db] : to0[db], pf[t], dvt[db]);
+            else dkt[db] = mfma(t ? tq1[db] : tq0[db], sf[t], dkt[db]);
+            if (m < kHalf) {
+                if (m & 1) tq1[m >> 1] = ln.tr_frag(Qc, qb, 1, m >> 1);
+                else to1[m >> 1] = ln.tr_frag(Oc, qb, 1, m >> 1);
+            } else {
+                // NS fragments and the 4 statistics reads over kHalf steps
+                const int r0 = (m - kHalf) * (NS + 4) / kHalf, r1 = (m - kHalf + 1) * (NS + 4) / kHalf;
+#pragma unroll
+                for (int r = r0; r < r1; ++r) {
+                    if (r < NS) rq[r] = ln.row_frag(Qx, qb ^ 1, r);
+                    else {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(
+                            Sx + 32 * (qb ^ 1) + 8 * (r - NS) + 4 * h);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s_init[4 * (r - NS) + e] = a[e];
+                    }
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp_acc[i] - dq[i]);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bf16x8 pf = cvt8(p + 8 * t);
-                const bf16x8 sf = cvt8(ds + 8 * t);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dvt[db] = mfma(ln.tr_frag(Oc, qb, t, db), pf, dvt[db]);
-                    dkt[db] = mfma(ln.tr_frag(Qc, qb, t, db), sf, dkt[db]);
-                }
+            if (qb == 1 && m == kHalf - 1) {
+                sync_tiles();
+                if (jt + 2 < jt1) copy_tile(jt + 2, Qc, Oc, Sc);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        sync_tiles();
     };
     if (jt0 < jt1) {
-        ln.copy(Qh, jt0 * BQ, Lq, Qb0, wave);
-        ln.copy(Oh, jt0 * BQ, Lq, Ob0, wave);
-        copy_stats(jt0, Sb0);
+        copy_tile(jt0, Qb0, Ob0, Sb0);
+        if (jt0 + 1 < jt1) copy_tile(jt0 + 1, Qb1, Ob1, Sb1);
         sync_tiles();
-        for (int jt = jt0; jt < jt1; jt += 2) {
-            step(jt, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
-            if (jt + 1 < jt1) step(jt + 1, Qb1, Ob1, Sb1, Qb0, Ob0, Sb0);
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) rq[s2] = ln.row_frag(Qb0, 0, s2);
+        read_stats(Sb0, 0, s_init);
+        using B0 = std::integral_constant<int, 0>;
+        using B1 = std::integral_constant<int, 1>;
+        // tiles in pairs (even tiles in buffer 0, odd in buffer 1), then a
+        // last odd one out: a loop body without a join keeps the carried
+        // registers in place
+        int jt = jt0;
+        for (; jt + 1 < jt1; jt += 2) {
+            block(jt, B0{}, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
+            block(jt, B1{}, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
+            block(jt + 1, B0{}, Qb1, Ob1, Sb1, Qb0, Ob0, Sb0);
+            block(jt + 1, B1{}, Qb1, Ob1, Sb1, Qb0, Ob0, Sb0);
+        }
+        if (jt < jt1) {
+            block(jt, B0{}, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
+            block(jt, B1{}, Qb0, Ob0, Sb0, Qb1, Ob1, Sb1);
         }
     }
     // dK = scale dS^T Q, dV = P^T dO; lane = key, rows = d
@@ -375,7 +456,7 @@ __global__ __launch_bounds__(64 * kQWaves)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                       const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-                      const float* __restrict__ lse2, const float* __restrict__ delta,
+                      const float* __restrict__ nlse, const float* __restrict__ ndelta,
                       uint16_t* __restrict__ dQ, int BH, int Lq, int Lk, int nqb, float c,
                       float scale)
 {
@@ -420,8 +501,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             of[s] = qi < Lq ? *reinterpret_cast<const bf16x8*>(Or + 16 * s + 8 * h) : bf16x8{};
         }
     }
-    const float lq = qi < Lq ? lse2[(size_t)bh * Lq + qi] : 0.f;
-    const float dq = qi < Lq ? delta[(size_t)bh * Lq + qi] : 0.f;
+    // this lane's query: c (-LSE / scale) = -LSE log2(e), and -Delta
+    const float lqc = qi < Lq ? nlse[(size_t)bh * Lq + qi] * c : 0.f;
+    const float nd = qi < Lq ? ndelta[(size_t)bh * Lq + qi] : 0.f;
     f32x16 dqt[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dqt[db] = f32x16{};
@@ -449,7 +531,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
             float p[16], ds[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, -lq));
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_acc[i], c, lqc));
             // Masks, on the blocks that need them (a wave-uniform test).  A
             // query past Lq needs none: its lane's column of dQ is never
             // stored.  Element i holds key k0 + off + 4h with off = 8 (i/4) +
@@ -463,7 +545,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp_acc[i] - dq);
+            for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp_acc[i] + nd);
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const bf16x8 sf = cvt8(ds + 8 * t);
@@ -496,7 +578,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        int B, int H, int Lq, int Lk, float scale, float* delta, float* lse2,
+                        int B, int H, int Lq, int Lk, float scale, float* ndelta, float* nlse,
                         hipStream_t stream)
 {
     const int BH = B * H;
@@ -504,7 +586,7 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
     constexpr int RPB = 256 / (D / 8);
     hipLaunchKernelGGL((fa_bwd_pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
                        0, stream, static_cast<const uint16_t*>(o),
-                       static_cast<const uint16_t*>(dout), lse, delta, lse2, rows);
+                       static_cast<const uint16_t*>(dout), lse, ndelta, nlse, rows, scale);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const float c = scale * kLog2e;
@@ -512,7 +594,7 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BH)),
                        dim3(64 * kKVWaves), 0, stream, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), lse2, delta,
+                       static_cast<const uint16_t*>(dout), nlse, ndelta,
                        static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), BH, Lq, Lk, nkb,
                        c, scale);
     err = hipGetLastError();
@@ -521,7 +603,7 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
     hipLaunchKernelGGL((fa_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)),
                        dim3(64 * kQWaves), 0, stream, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), lse2, delta,
+                       static_cast<const uint16_t*>(dout), nlse, ndelta,
                        static_cast<uint16_t*>(dq), BH, Lq, Lk, nqb, c, scale);
     return hipGetLastError();
 }
@@ -533,15 +615,15 @@ bool bwd_supported(int d) { return d == 64 || d == 128; }
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       int B, int H, int Lq, int Lk, int d, bool causal, float scale,
-                      float* delta, float* lse2, hipStream_t stream)
+                      float* ndelta, float* nlse, hipStream_t stream)
 {
     switch (d) {
     case 64:
-        return causal ? launch_bwd_d<64, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream)
-                      : launch_bwd_d<64, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream);
+        return causal ? launch_bwd_d<64, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, ndelta, nlse, stream)
+                      : launch_bwd_d<64, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, ndelta, nlse, stream);
     case 128:
-        return causal ? launch_bwd_d<128, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream)
-                      : launch_bwd_d<128, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, delta, lse2, stream);
+        return causal ? launch_bwd_d<128, true>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, ndelta, nlse, stream)
+                      : launch_bwd_d<128, false>(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, scale, ndelta, nlse, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -40,11 +40,11 @@ hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o
 // Backward (bf16): head dims with a backward instantiation.
 bool bwd_supported(int d);
 
-// Backward: Delta and LSE * log2(e) into delta / lse2 ([B*H][Lq] fp32 each,
+// Backward: -Delta and -LSE / scale into ndelta / nlse ([B*H][Lq] fp32 each,
 // caller-provided), then dK/dV and dQ; three kernels on `stream`.
 hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o,
                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
                       int B, int H, int Lq, int Lk, int d, bool causal, float scale,
-                      float* delta, float* lse2, hipStream_t stream);
+                      float* ndelta, float* nlse, hipStream_t stream);
 
 }  // namespace fa

@@ -57,7 +57,10 @@ def check_grads(got, ref, label):
     for g, r, name in zip(got, ref, ("dQ", "dK", "dV")):
         gw = widen(g)
         assert np.isfinite(gw).all(), f"{label}: non-finite {name}"
-        scale = float(np.abs(r).max())
+        # an exactly zero gradient (a single visible key gives dS = 0) is held
+        # to the bar of a unit-sized one: the GPU's dP - Delta is rounding
+        # noise there
+        scale = max(float(np.abs(r).max()), 1.0 if not np.abs(r).max() else 0.0)
         err = float(np.abs(gw - r).max())
         say(f"{label}: {name} max|err| {err:.3e} = {err / scale:.2e} x max|ref| (bar {GRAD_REL})")
         assert err <= GRAD_REL * scale, f"{label}: {name} error {err} vs max {scale}"
@@ -76,7 +79,8 @@ def bwd_case(seed, B, H, Lq, Lk, d, causal, sigma_qk=1.0):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Lq,Lk,d", [(128, 128, 64), (300, 300, 128), (257, 500, 128),
-                                     (500, 257, 64), (130, 70, 128), (64, 1000, 128)])
+                                     (500, 257, 64), (130, 70, 128), (64, 1000, 128),
+                                     (20, 45, 128), (1, 33, 64)])
 def test_bwd_small(causal, Lq, Lk, d):
     bwd_case(61, 1, 2, Lq, Lk, d, causal)
 
