@@ -26,7 +26,7 @@ class Workload:
     Lq: int
     Lk: int
     d: int
-    dtype: str            # "bf16" or "fp32"
+    dtype: str            # "bf16", "fp32" or "fp8" (E4M3 codes + descales)
     modes: tuple          # subset of ("noncausal", "causal", "window", "splitkv")
     seed: int
     sigma_qk: float = 1.0
@@ -45,7 +45,7 @@ class Workload:
         return float(np.float32(1.0) / np.sqrt(np.float32(self.d)))
 
 
-# The five synthetic workloads (seeds 1..5, drawn in the order Q, K, V).
+# The synthetic workloads (one seed each, drawn in the order Q, K, V).
 WORKLOADS = {
     "tiny_fp32": Workload("tiny_fp32", 1, 2, 128, 128, 64, "fp32",
                           ("noncausal", "causal"), 1),
@@ -70,6 +70,11 @@ WORKLOADS = {
     "bf16_longkv_512x64k_d128": Workload("bf16_longkv_512x64k_d128", 1, 16, 512,
                                          65536, 128, "bf16", ("splitkv",), 7,
                                          splits=8),
+    # FP8 E4M3 inputs (per-tensor descale) at the 16K causal shape, the
+    # pages' FP8 variant ("Flash Attention 原理与实现详解" (tbr8.org), section
+    # 4.3 "FP8 支持")
+    "fp8_causal_16k_d128": Workload("fp8_causal_16k_d128", 1, 16, 16384, 16384, 128,
+                                    "fp8", ("causal",), 8),
 }
 
 
@@ -132,6 +137,65 @@ def make_grad(seed: int, B: int, H: int, Lq: int, d: int) -> np.ndarray:
     return round_to_bf16_bits(rng.standard_normal((B, H, Lq, d), dtype=np.float32))
 
 
+# ---- FP8 inputs (OCP FP8 E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa
+# bits; no infinities; S.1111.111 is NaN; largest finite 448) ------------------
+def _e4m3_positive_table() -> np.ndarray:
+    """Values of the codes 0..126 (all finite non-negative ones), ascending."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+_E4M3_POS = _e4m3_positive_table()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> exact float64 values (NaN for the NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag = c & 0x7F
+    val = np.where(mag == 0x7F, np.nan, _E4M3_POS[np.minimum(mag, 126)])
+    return np.where(c & 0x80, -val, val)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 codes, round to nearest, ties to even; |x| <= 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    assert np.isfinite(a).all() and (a <= 448.0).all()
+    hi = np.minimum(np.searchsorted(_E4M3_POS, a, side="left"), 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(_E4M3_POS[hi] == a, hi, pick)
+    return (pick | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor quantisation: descale = max|x| / 448 (fp32), codes =
+    e4m3(x / descale).  The value a code stands for is decode(code) *
+    descale."""
+    amax = float(np.abs(x).max())
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    y = np.asarray(x, dtype=np.float64) / descale
+    return e4m3_encode(np.clip(y, -448.0, 448.0)), descale
+
+
+def make_inputs_fp8(seed: int, B: int, H: int, Lq: int, Lk: int, d: int,
+                    sigma_qk: float = 1.0, sigma_v: float = 1.0):
+    """Return (q8, k8, v8, (q_descale, k_descale, v_descale)): the same fp32
+    Gaussian draw as make_inputs, each tensor quantised to E4M3 codes with its
+    own per-tensor descale factor."""
+    q, k, v = draw(seed, B, H, Lq, Lk, d, sigma_qk, sigma_v)
+    (q8, qd), (k8, kd), (v8, vd) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+    return q8, k8, v8, (qd, kd, vd)
+
+
+def widen_fp8(codes: np.ndarray, descale: float) -> np.ndarray:
+    """E4M3 codes and their descale -> the exact float64 values they stand
+    for (decode(code) * descale, exact in float64)."""
+    return e4m3_decode(codes) * float(descale)
+
+
 def widen(x: np.ndarray) -> np.ndarray:
     """Storage array (bf16 bits or fp32) -> exact float64 values."""
     if x.dtype == np.uint16:
@@ -140,5 +204,9 @@ def widen(x: np.ndarray) -> np.ndarray:
 
 
 def workload_inputs(w: Workload):
+    """(q, k, v) storage arrays; fp8 workloads also return the descales as a
+    fourth element."""
+    if w.dtype == "fp8":
+        return make_inputs_fp8(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, w.sigma_qk, w.sigma_v)
     return make_inputs(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, w.dtype,
                        w.sigma_qk, w.sigma_v)

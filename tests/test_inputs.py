@@ -42,10 +42,24 @@ def test_sigma_and_widen():
 
 
 def test_workload_table():
-    assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5, 6, 7]
+    assert [w.seed for w in WORKLOADS.values()] == [1, 2, 3, 4, 5, 6, 7, 8]
+    w = WORKLOADS["fp8_causal_16k_d128"]
+    assert (w.dtype, w.B, w.H, w.Lq, w.Lk, w.d, w.modes) == ("fp8", 1, 16, 16384, 16384, 128, ("causal",))
     assert WORKLOADS["bf16_longkv_512x64k_d128"].splits == 8
     w = WORKLOADS["bf16_window1k_16k_d128"]
     assert w.window == (1024, 0) and w.window_abi == (1024, 0) and w.modes == ("window",)
     w = WORKLOADS["bf16_peaky_d256_ragged"]
     assert (w.Lq, w.Lk, w.d, w.sigma_qk) == (8000, 8192, 256, 3.0)
     assert np.float32(WORKLOADS["bf16_4k_d128"].scale) == np.float32(1 / np.sqrt(np.float32(128)))
+
+
+def test_fp8_inputs_follow_the_bf16_draw():
+    """The FP8 inputs quantise the same Gaussian draw, per tensor."""
+    from seeded_inputs import make_inputs_fp8, widen_fp8
+    q8, k8, v8, (qd, kd, vd) = make_inputs_fp8(9, 1, 2, 50, 60, 16)
+    qf, kf, vf = draw(9, 1, 2, 50, 60, 16)
+    for c, ds, x in ((q8, qd, qf), (k8, kd, kf), (v8, vd, vf)):
+        assert c.dtype == np.uint8 and c.shape == x.shape
+        assert ds == np.float32(np.abs(x).max() / 448.0)
+        y = widen_fp8(c, ds)
+        assert np.abs(y - x).max() <= 2.0 ** -4 * np.abs(x).max()
