@@ -12,6 +12,10 @@ benchmark harness).  The roofline object prices that against MI355X's dense
 bf16 MFMA peak (2.5 PFLOP/s).  The CPU baseline times the fp64 oracle on a
 bounded sample of the same workload (whole heads) on this host's cores; it
 is a reported baseline only.
+
+``--workload fp8_causal_16k_d128`` runs the FP8 (E4M3) forward, fa_fwd_fp8,
+priced against the dense FP8 MFMA peak (5.0 PFLOP/s); its CPU baseline is
+the FP8 oracle (the blocked algorithm with E4M3-rounded P).
 """
 from __future__ import annotations
 
@@ -29,12 +33,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s (bf16, causal & non-causal) and % of MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}   # MI355X dense MFMA / fp32
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA / fp32
 DEFAULT_WORKLOAD = "bf16_causal_16k_d128"
 KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                              "fa_fwd_kernel.hip")
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                                  "fa_bwd_kernel.hip")
+FP8_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
+                                 "fa_fp8_kernel.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -53,7 +59,7 @@ def kernel_source_hash(path: str = None) -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, backward: bool = False):
+def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = False):
     """HBM bytes per call from the committed rocprofv3 counter summary for
     this workload and pass, or None if absent or taken on a different
     kernel source."""
@@ -61,12 +67,17 @@ def traffic_from_profiles(workload: str, backward: bool = False):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if fp8:
+        h3 = re.search(r"fp8_kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+        if not t or not h3 or h3.group(1) != kernel_source_hash(FP8_KERNEL_SOURCE):
+            return None
+        return float(t.group(1))
+    h = re.search(r"(?<![a-z0-9_])kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if backward:
         h2 = re.search(r"bwd_kernel_source_sha256_16:\s*([0-9a-f]+)", text)
         if not h2 or h2.group(1) != kernel_source_hash(BWD_KERNEL_SOURCE):
             return None
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
@@ -134,6 +145,48 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
         "seconds": spent,
         "sample_flops": fl,
     }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "slices": done}
+
+
+def cpu_baseline_fp8(w, causal, q8, k8, v8, ds, gpu_out, budget_s=15.0, max_heads=None):
+    """Time the FP8 oracle (the blocked algorithm with E4M3-rounded P, at the
+    kernel's key-tile size) on whole (batch, head) slices until budget_s of
+    host time is spent; report the GPU result's distance to it and to the
+    exact definition on that sample."""
+    import exact_io_aware_08_amd as fa
+    from oracle import attention_fp8_blocked, attention_ref, default_workers, fp8_flops
+    from seeded_inputs import widen, widen_fp8
+    block = fa.tile_config("fp8", w.d)[1]
+    O_gpu, L_gpu = gpu_out
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if max_heads:
+        slices = slices[:max_heads]
+    spent, done, eb, ee, el = 0.0, 0, 0.0, 0.0, 0.0
+    for b, h in slices:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        qs, ks, vs = (widen_fp8(x[sl], s) for x, s in zip((q8, k8, v8), ds))
+        t0 = time.perf_counter()
+        O_blk, L_blk = attention_fp8_blocked(qs, ks, vs, causal, w.scale, block)
+        spent += time.perf_counter() - t0
+        done += 1
+        og = widen(O_gpu[sl])
+        eb = max(eb, float(np.abs(og - O_blk).max()))
+        el = max(el, float(np.abs(L_gpu[sl].astype(np.float64) - L_blk).max()))
+        if done == 1:
+            rows = np.arange(0, w.Lq, max(1, w.Lq // 256))
+            O_ex, _ = attention_ref(qs, ks, vs, causal, w.scale, rows=rows,
+                                    workers=default_workers())
+            ee = float(np.abs(og[:, :, rows] - O_ex).max())
+        if spent >= budget_s:
+            break
+    fl = done * fp8_flops(w.Lq, w.Lk, w.d, causal)
+    return {
+        "value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{done} of {w.B * w.H} (batch, head) slices, all {w.Lq} rows each, "
+                   f"fp64 numpy blocked FP8 oracle (one process, BLAS threads per numpy "
+                   f"default), {spent:.2f} s wall"),
+        "seconds": spent,
+    }, {"max_abs_err_O_vs_blocked_fp8": eb, "max_abs_err_LSE": el,
+        "max_abs_err_O_vs_exact_sampled_rows": ee, "slices": done}
 
 
 def cpu_baseline_bwd(w, causal, q, k, v, do, grads, budget_s=15.0, max_heads=None):
@@ -226,10 +279,17 @@ def main(argv=None):
     mode = a.mode or w.modes[0]
     causal = mode == "causal" or (mode == "bwd" and "causal" in w.modes)
     window = w.window if mode == "window" else None
+    fp8 = w.dtype == "fp8"
+    if fp8 and mode not in ("causal", "noncausal"):
+        raise SystemExit("the FP8 forward has causal and non-causal modes only")
     log(f"bench: workload {w.name} mode {mode} steps {a.steps} warmup {a.warmup}")
-    q, k, v = workload_inputs(w)
-    qd, kd, vd = to_device(q), to_device(k), to_device(v)
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if fp8:
+        q, k, v, descales = workload_inputs(w)
+        qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q, k, v))
+    else:
+        q, k, v = workload_inputs(w)
+        qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    tdt = torch.float32 if w.dtype == "fp32" else torch.bfloat16
     od = torch.empty((w.B, w.H, w.Lq, w.d), dtype=tdt, device="cuda")
     ld = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -251,6 +311,10 @@ def main(argv=None):
         fn = fa.fa_bwd
         args = (qd, kd, vd, od, ld, dod, dqd, dkd, dvd, w.B, w.H, w.Lq, w.Lk, w.d,
                 int(causal), w.scale, ws, nbytes, stream)
+    elif fp8:
+        fn = fa.fa_fwd_fp8
+        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal), w.scale,
+                *descales, stream)
     elif window is not None:
         fn = fa.fa_fwd_window
         args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, *w.window_abi,
@@ -318,6 +382,13 @@ def main(argv=None):
         cpu, parity = cpu_baseline_bwd(w, causal, q, k, v, do, grads, a.cpu_budget, a.cpu_heads)
         log(f"bench: oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores "
             f"-> {cpu['value'] * 1e3:.2f} GFLOP/s; parity on sample {parity}")
+    elif not a.no_cpu_baseline and fp8:
+        gpu_out = (od.view(torch.int16).cpu().numpy().view(np.uint16), ld.cpu().numpy())
+        log("bench: CPU oracle baseline (FP8) ...")
+        cpu, parity = cpu_baseline_fp8(w, causal, q, k, v, descales, gpu_out, a.cpu_budget,
+                                       a.cpu_heads)
+        log(f"bench: oracle {cpu['seconds']:.2f} s -> {cpu['value'] * 1e3:.2f} GFLOP/s; "
+            f"parity on sample {parity}")
     elif not a.no_cpu_baseline:
         o_np = od.view(torch.int16).cpu().numpy().view(np.uint16) \
             if w.dtype == "bf16" else od.cpu().numpy()
@@ -339,7 +410,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8_e4m3" if fp8 else w.dtype,
         "data": "synthetic",
         "pct_of_mfma_peak": round(100 * value / peak, 3),
         "config": {"workload": f"{w.name} ({mode})", "B": w.B, "H": w.H,
@@ -351,7 +422,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 5),
-                     "traffic": traffic_from_profiles(w.name, backward),
+                     "traffic": traffic_from_profiles(w.name, backward, fp8),
                      "kernel_ms": round(ms_kernel, 5),
                      "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None if cpu is None else {

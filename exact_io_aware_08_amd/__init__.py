@@ -24,7 +24,7 @@ STATUS_NAMES = {
     8: "FA_ERR_WORKSPACE",
 }
 # every function the C header declares
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_splitkv",
            "fa_splitkv_workspace_size", "fa_bwd", "fa_bwd_workspace_size",
            "fa_status_string", "fa_abi_version", "fa_tile_config")
 
@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_f32.argtypes = sig
     lib.fa_fwd_f32.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_window.restype = i
     sz = ctypes.c_size_t
@@ -109,10 +111,11 @@ def abi_version() -> int:
 
 
 def tile_config(dtype: str, d: int):
-    """(block_m, block_n, threads) the library uses for dtype 'bf16'/'fp32'."""
+    """(block_m, block_n, threads) the library uses for dtype 'bf16', 'fp32'
+    or 'fp8'."""
     lib = load_library()
     bm, bn, th = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    st = lib.fa_tile_config(0 if dtype == "bf16" else 1, int(d),
+    st = lib.fa_tile_config({"bf16": 0, "fp32": 1, "fp8": 2}[dtype], int(d),
                             ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(th))
     if st != FA_OK:
         raise FAError(st, status_string(st))
@@ -141,6 +144,19 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream=None):
     """fp32 forward through the C ABI (``fa_fwd_f32``)."""
     return _call(load_library().fa_fwd_f32, q, k, v, o, lse, B, H, Lq, Lk, d,
                  causal, scale, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, q_descale, k_descale,
+               v_descale, stream=None):
+    """FP8 (E4M3) forward through the C ABI (``fa_fwd_fp8``): q, k, v hold
+    E4M3 codes (one byte each) standing for code * descale; o is bf16."""
+    st = load_library().fa_fwd_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Lq), int(Lk),
+        int(d), int(causal), float(scale), float(q_descale), float(k_descale),
+        float(v_descale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
 
 
 def fa_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, window_left, window_right,

@@ -148,6 +148,41 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                Lk, d, ms, m, scale, stream);
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Lq, int Lk, int d, int causal, float scale,
+               float q_descale, float k_descale, float v_descale, hipStream_t stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return FA_ERR_SHAPE;
+    fa::TileConfig tc;
+    if (!fa::fp8_tile_config(d, &tc)) return FA_ERR_UNSUPPORTED_D;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return FA_ERR_ALIGN;
+    for (float x : {scale, q_descale, k_descale, v_descale})
+        if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
+    // the exponent factor of S: scale * q_descale * k_descale * log2(e)
+    const double cd = (double)scale * q_descale * k_descale * 1.4426950408889634;
+    const float c = (float)cd;
+    if (!std::isfinite(c) || !(c > 0.f)) return FA_ERR_SCALE;
+    if (causal != 0 && causal != 1) return FA_ERR_ARG;
+    const long long bh = (long long)B * H;
+    const long long grid = (((long long)Lq + tc.block_m - 1) / tc.block_m) * bh;
+    if (bh > (1LL << 30) || grid > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if ((long long)Lq * d > 0x7fffffffLL || (long long)Lk * d > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
+    const std::size_t qbytes = (std::size_t)bh * Lq * d;        // E4M3: 1 byte
+    const std::size_t kbytes = (std::size_t)bh * Lk * d;
+    const std::size_t obytes = (std::size_t)bh * Lq * d * 2;    // bf16
+    const std::size_t lbytes = (std::size_t)bh * Lq * sizeof(float);
+    if (overlaps(o, obytes, q, qbytes) || overlaps(o, obytes, k, kbytes) ||
+        overlaps(o, obytes, v, kbytes) || overlaps(lse, lbytes, q, qbytes) ||
+        overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
+        overlaps(lse, lbytes, o, obytes))
+        return FA_ERR_ARG;
+    const hipError_t err = fa::launch_fwd_fp8(q, k, v, o, lse, B, H, Lq, Lk, d, causal == 1, c,
+                                              v_descale, stream);
+    return err == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                float* lse, int B, int H, int Lq, int Lk, int d, int causal,
                float scale, hipStream_t stream) {
@@ -250,10 +285,11 @@ const char* fa_status_string(int status) {
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
 int fa_tile_config(int dtype, int d, int* block_m, int* block_n, int* threads) {
-    if (dtype != 0 && dtype != 1) return FA_ERR_ARG;
+    if (dtype < 0 || dtype > 2) return FA_ERR_ARG;
     fa::TileConfig tc;
-    if (!fa::tile_config(dtype == 0 ? fa::DType::BF16 : fa::DType::F32, d, &tc))
-        return FA_ERR_UNSUPPORTED_D;
+    const bool ok = dtype == 2 ? fa::fp8_tile_config(d, &tc)
+                               : fa::tile_config(dtype == 0 ? fa::DType::BF16 : fa::DType::F32, d, &tc);
+    if (!ok) return FA_ERR_UNSUPPORTED_D;
     if (block_m) *block_m = tc.block_m;
     if (block_n) *block_n = tc.block_n;
     if (threads) *threads = tc.threads;

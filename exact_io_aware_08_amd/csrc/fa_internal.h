@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI shim (fa_api.cpp) and the kernel
-// translation unit (fa_fwd_kernel.hip).  Not installed, not part of the ABI.
+// translation units (fa_fwd_kernel.hip, fa_fp8_kernel.hip, fa_bwd_kernel.hip).
+// Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -36,6 +37,15 @@ hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* 
 hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int Lq, int Lk, int d, bool causal, float scale,
                             int nsplit, float* opart, float* lpart, hipStream_t stream);
+
+// FP8 (E4M3) forward: tile geometry for head dim d (false: no instantiation).
+bool fp8_tile_config(int d, TileConfig* out);
+
+// FP8 forward: q, k, v E4M3 codes, o bf16, lse fp32.  c = scale * q_descale *
+// k_descale * log2(e) (the exponent factor of S), vd = v_descale.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Lq, int Lk, int d, bool causal, float c, float vd,
+                          hipStream_t stream);
 
 // Backward (bf16): head dims with a backward instantiation.
 bool bwd_supported(int d);

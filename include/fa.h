@@ -49,7 +49,8 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd */
+#define FA_ABI_VERSION 5   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd;
+                              5: fa_fwd_fp8 */
 
 enum fa_status {
     FA_OK = 0,
@@ -164,6 +165,31 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int d, int causal, float scale, void* workspace, size_t workspace_bytes,
            hipStream_t stream);
 
+/*
+ * FP8 forward: the same operation on FP8 inputs, the pages' FP8 variant
+ * ("Flash Attention 原理与实现详解" (tbr8.org), section 4.3 "FP8 支持"; the
+ * page warns that it loses more precision, section 6.1 "精度问题").
+ *   q, k, v   : OCP FP8 E4M3 codes (1 byte each: sign, 4 exponent bits with
+ *               bias 7, 3 mantissa bits; 448 the largest finite value),
+ *               [B, H, Lq, d] / [B, H, Lk, d]; the value of a code is
+ *               decode(code) * q_descale (k_descale, v_descale for k, v)
+ *   o         : bf16 [B, H, Lq, d];  lse: fp32 [B, H, Lq], natural log
+ *   d         : 128 (other values: FA_ERR_UNSUPPORTED_D)
+ *   descales  : finite and > 0, and scale * q_descale * k_descale finite and
+ *               > 0 (else FA_ERR_SCALE)
+ * S = scale * q_descale * k_descale * (Q K^T) from the codes (their products
+ * are exact, fp32 accumulation); the second product takes P multiplied by
+ * 2^8 and rounded to E4M3 (nearest even), while the row sum uses the
+ * unrounded P, so o differs from the exact result by at most
+ * 2^-4 sum_j P_ij |v_jd| + 2^-18 sum_j |v_jd| / l_i (P the exact softmax
+ * weights, l_i = sum_j exp(s_ij - max_j s_ij)) plus the bf16 rounding of o;
+ * lse keeps fp32 accuracy.  One kernel on `stream`; layout, ownership,
+ * overlap rules and errors as fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int Lq, int Lk, int d, int causal, float scale,
+               float q_descale, float k_descale, float v_descale, hipStream_t stream);
+
 /* Workspace bytes fa_bwd needs (0 for B, H or Lq < 1).  Host-only. */
 size_t fa_bwd_workspace_size(int B, int H, int Lq);
 
@@ -176,7 +202,8 @@ int fa_abi_version(void);
 /*
  * Tile geometry the library uses for (dtype, d): query rows per workgroup
  * (block_m), keys per K/V tile (block_n) and threads per workgroup.  dtype
- * is 0 for bf16, 1 for fp32.  Returns FA_OK, or FA_ERR_UNSUPPORTED_D /
+ * is 0 for bf16, 1 for fp32, 2 for FP8 E4M3 (fa_fwd_fp8).  Returns FA_OK,
+ * or FA_ERR_UNSUPPORTED_D /
  * FA_ERR_ARG for an unknown combination.  Host-only; makes no HIP call.
  */
 int fa_tile_config(int dtype, int d, int* block_m, int* block_n,

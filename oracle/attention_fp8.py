@@ -36,6 +36,17 @@ Two functions pin such a kernel from two sides:
       most 2^-4 P_j (normal range) or 2^-18 (below it), so
           |O_fp8 - O|_id <= 2^-4 sum_j P_ij |v_jd| + 2^-18 sum_j |v_jd| / l_i
       with P_ij = p_j / l_i the exact softmax weights.
+
+Both take an optional bound on the error of S itself, s_err: |s~_ij - s_ij|
+<= s_err * scale * sum_t |q_it| |k_jt| (a matrix unit that accumulates the
+products with less than fp32 precision).  With D_i = max_j of that bound,
+every p_j moves by a factor within e^(+-D_i) (its score and the max both
+move), which adds (e^(2 D_i) - 1)(sum_j P_ij |v_jd| + |O_id|) to the bound
+and scales its rounding terms by e^(2 D_i); the blocked algorithm then also
+returns an allowance: that continuous term plus, for every P whose 2^8
+multiple lies within that relative window of an E4M3 rounding midpoint,
+one E4M3 spacing of it (it may round the other way), carried through the
+rescaling and normalisation like O itself.
 """
 from __future__ import annotations
 
@@ -67,31 +78,54 @@ def _causal_visible(rows, keys):
     return keys[None, :] <= rows[:, None]
 
 
+def _e4m3_midpoint_gap(x):
+    """For x >= 0 (<= 448): distance to the nearest E4M3 rounding midpoint,
+    and the E4M3 spacing at x (the change of a flipped rounding)."""
+    _, e2 = np.frexp(x)
+    e = np.maximum(e2 - 1, -6)
+    spacing = np.ldexp(1.0, e - 3)
+    frac = x / spacing - np.floor(x / spacing)
+    return np.abs(frac - 0.5) * spacing, spacing
+
+
 def attention_fp8_blocked(q, k, v, causal: bool, scale: float, block: int,
-                          round_p: bool = True):
+                          round_p: bool = True, rows=None, s_err=None, s_noise=None):
     """The tiled online softmax with P rounded to E4M3 (see module doc).
 
     q [B,H,Lq,d], k, v [B,H,Lk,d]: the dequantised float64 values.  Keys are
     visited in blocks of `block`, in ascending order; a block with no visible
     key for a row changes nothing for it.  round_p=False skips the rounding
-    (then the result is the exact definition, up to fp64 rounding).
-    Returns O [B,H,Lq,d], LSE [B,H,Lq] (natural log)."""
+    (then the result is the exact definition, up to fp64 rounding).  rows:
+    optional query indexes to evaluate (default all).  s_err: also return the
+    per-element allowance for an S error bounded as in the module doc.
+    s_noise: optional [B,H,R,Lk] additions to s (natural units), to test that
+    allowance.
+    Returns O [B,H,R,d], LSE [B,H,R] (natural log) for the R rows, and the
+    allowance [B,H,R,d] when s_err is given."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
-    O = np.zeros((B, H, Lq, d))
-    LSE = np.zeros((B, H, Lq))
-    rows = np.arange(Lq)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    R = len(rows)
+    O = np.zeros((B, H, R, d))
+    LSE = np.zeros((B, H, R))
+    ALLOW = np.zeros((B, H, R, d)) if s_err is not None else None
     for b in range(B):
         for h in range(H):
-            m = np.full(Lq, -np.inf)          # running max of s (natural units)
-            l = np.zeros(Lq)                  # running sum of unrounded 2^8 P
-            acc = np.zeros((Lq, d))           # running sum of rounded 2^8 P times V
+            qr = q[b, h, rows]
+            m = np.full(R, -np.inf)           # running max of s (natural units)
+            l = np.zeros(R)                   # running sum of unrounded 2^8 P
+            acc = np.zeros((R, d))            # running sum of rounded 2^8 P times V
+            flip = np.zeros((R, d))           # running sum of possible flips times |V|
+            if s_err is not None:
+                sabs = s_err * abs(scale) * (np.abs(qr) @ np.abs(k[b, h]).T)
             for j0 in range(0, Lk, block):
                 keys = np.arange(j0, min(j0 + block, Lk))
-                s = scale * (q[b, h] @ k[b, h, keys].T)
+                s = scale * (qr @ k[b, h, keys].T)
+                if s_noise is not None:
+                    s = s + s_noise[b, h][:, keys]
                 vis = _causal_visible(rows, keys) if causal else np.ones(s.shape, bool)
                 s = np.where(vis, s, -np.inf)
                 m_new = np.maximum(m, s.max(axis=1))
@@ -102,32 +136,61 @@ def attention_fp8_blocked(q, k, v, causal: bool, scale: float, block: int,
                 pr = e4m3_round(p) if round_p else p
                 l = l * alpha + p.sum(axis=1)
                 acc = acc * alpha[:, None] + pr @ v[b, h, keys]
+                if s_err is not None:
+                    # a relative window of e^(2 D) - 1 around each 2^8 P, plus
+                    # fp32 slack for the exponent argument and exp2
+                    win = np.expm1(2.0 * sabs.max(axis=1, keepdims=True)) + 2.0 ** -19
+                    gap, spacing = _e4m3_midpoint_gap(p)
+                    near = vis & (gap <= p * win)
+                    flip = flip * alpha[:, None] + np.where(near, spacing, 0.0) @ np.abs(v[b, h, keys])
                 m = m_new
             O[b, h] = acc / l[:, None]
             LSE[b, h] = m + np.log(l) - P_SHIFT * math.log(2.0)
+            if s_err is not None:
+                Dm = sabs.max(axis=1)[:, None]
+                pw = np.abs(pr_weights(qr, k[b, h], v[b, h], rows, causal, scale))
+                ALLOW[b, h] = flip / l[:, None] + np.expm1(2.0 * Dm) * (pw + np.abs(O[b, h]))
+    if s_err is not None:
+        return O, LSE, ALLOW
     return O, LSE
 
 
-def fp8_error_bound(q, k, v, causal: bool, scale: float):
-    """Per-element bound on |O_fp8 - O_exact| from rounding P to E4M3 (see
-    module doc); fp64, shape of O.  Output rounding is not included."""
+def pr_weights(qr, k, v, rows, causal, scale):
+    """sum_j P_ij |v_jd| with the exact softmax weights of the given rows."""
+    Lk = k.shape[0]
+    s = scale * (qr @ k.T)
+    vis = _causal_visible(rows, np.arange(Lk)) if causal else np.ones(s.shape, bool)
+    s = np.where(vis, s, -np.inf)
+    p = np.where(vis, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
+    return (p / p.sum(axis=1, keepdims=True)) @ np.abs(v)
+
+
+def fp8_error_bound(q, k, v, causal: bool, scale: float, rows=None, s_err: float = 0.0):
+    """Per-element bound on |O_fp8 - O_exact| from rounding P to E4M3, and
+    from an S error bounded by s_err (see module doc); fp64, shape of O (of
+    the selected rows).  Output rounding is not included."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
-    out = np.zeros((B, H, Lq, d))
-    rows = np.arange(Lq)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    out = np.zeros((B, H, len(rows), d))
     keys = np.arange(Lk)
     for b in range(B):
         for h in range(H):
-            s = scale * (q[b, h] @ k[b, h].T)
+            s = scale * (q[b, h, rows] @ k[b, h].T)
             vis = _causal_visible(rows, keys) if causal else np.ones(s.shape, bool)
             s = np.where(vis, s, -np.inf)
             p = np.where(vis, np.exp(s - s.max(axis=1, keepdims=True)), 0.0)
             l = p.sum(axis=1, keepdims=True)
             av = np.abs(v[b, h])
-            out[b, h] = 2.0 ** -4 * (p / l) @ av + 2.0 ** -18 * (vis.astype(np.float64) @ av) / l
+            pw = (p / l) @ av
+            g = np.exp(2.0 * s_err * abs(scale) * (np.abs(q[b, h, rows]) @ np.abs(k[b, h]).T).max(
+                axis=1, keepdims=True))
+            O = (p / l) @ v[b, h]
+            out[b, h] = (g * (2.0 ** -4 * pw + 2.0 ** -18 * (vis.astype(np.float64) @ av) / l)
+                         + (g - 1.0) * (pw + np.abs(O)))
     return out
 
 

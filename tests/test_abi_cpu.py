@@ -62,6 +62,11 @@ def test_tile_config():
             assert th in (128, 256, 512) and bm % (th // 64 * 32) == 0
     with pytest.raises(fa.FAError):
         fa.tile_config("bf16", 96)
+    bm, bn, th = fa.tile_config("fp8", 128)
+    assert bm % 32 == 0 and bn % 64 == 0 and bm % (th // 64 * 32) == 0
+    for d in (64, 256):
+        with pytest.raises(fa.FAError):
+            fa.tile_config("fp8", d)
 
 
 def _st(fn, **kw):
@@ -189,3 +194,33 @@ def test_bwd_validation_errors():
     assert _st_bwd(workspace_bytes=fa.bwd_workspace_size(1, 2, 128) - 1) == 8
     assert _st_bwd(dk=Q + 64) == 6         # an output overlapping an input
     assert _st_bwd(dv=DK + 16) == 6        # two outputs overlapping
+
+
+def _st_fp8(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Lq=128, Lk=128, d=128,
+                causal=0, scale=0.125, q_descale=0.01, k_descale=0.02, v_descale=0.03)
+    args.update(kw)
+    try:
+        fa.fa_fwd_fp8(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+def test_fp8_validation_errors():
+    assert _st_fp8(v=0) == 1
+    for bad in ({"B": 0}, {"Lq": 0}, {"Lk": -3}):
+        assert _st_fp8(**bad) == 2
+    for d in (64, 96, 256):
+        assert _st_fp8(d=d) == 3
+    assert _st_fp8(q=Q + 8) == 4
+    for name in ("scale", "q_descale", "k_descale", "v_descale"):
+        for x in (0.0, -1.0, math.inf, math.nan):
+            assert _st_fp8(**{name: x}) == 5
+    # the combined exponent factor overflows / underflows fp32
+    assert _st_fp8(q_descale=1e30, k_descale=1e30) == 5
+    assert _st_fp8(q_descale=1e-30, k_descale=1e-30) == 5
+    assert _st_fp8(causal=3) == 6
+    # o is bf16 (2 bytes per element) over 1-byte inputs: o = [Q, Q + 2 |q|)
+    assert _st_fp8(k=Q + 2 * 2 * 128 * 128 - 16, o=Q, q=O) == 6
+    assert _st_fp8(lse=V + 2 * 128 * 128 - 16) == 6

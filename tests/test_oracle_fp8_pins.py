@@ -12,6 +12,9 @@ codec (seeded_inputs) to things other than themselves.
   a two-key row whose rounded P is a known E4M3 tie.
 * The derived error bound holds on random and peaky inputs and is nearly
   attained where it should be.
+* With an S error inside the stated bound (random noise on the scores),
+  the blocked result stays within its allowance and the exact definition's
+  bound.
 * Planted mistakes in copies of the oracle (dropped 2^8 shift, l from the
   rounded P, no rescale, ties away from zero) are each rejected.
 """
@@ -200,6 +203,34 @@ def test_rounding_error_within_bound(causal, sigma, block):
     assert (np.abs(O - Or) <= bound + 1e-12).all()
     assert np.abs(L - Lr).max() <= 1e-12          # l comes from the unrounded P
     assert np.abs(O - Or).max() > 0               # the rounding does act
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("s_err", [2.0 ** -13, 2.0 ** -8])
+def test_s_error_allowance_and_bound(causal, s_err):
+    """S perturbed within the stated bound (random noise up to
+    s_err * scale * sum|q||k| per score): the blocked result moves by no more
+    than its allowance, and stays within the exact definition's bound."""
+    q, k, v = fp8_case(15, 1, 2, 120, 150, 32)
+    scale = 1 / math.sqrt(32)
+    O, L, allow = f8.attention_fp8_blocked(q, k, v, causal, scale, 32, s_err=s_err)
+    O0, _ = f8.attention_fp8_blocked(q, k, v, causal, scale, 32)
+    assert np.array_equal(O, O0)
+    Oe, _ = attention_ref(q, k, v, causal, scale)
+    bound = f8.fp8_error_bound(q, k, v, causal, scale, s_err=s_err)
+    dmax = s_err * scale * np.einsum("bhid,bhjd->bhij", np.abs(q), np.abs(k))
+    rng = np.random.default_rng(4)
+    moved = 0.0
+    for _ in range(4):
+        noise = rng.uniform(-1, 1, dmax.shape) * dmax
+        On, Ln = f8.attention_fp8_blocked(q, k, v, causal, scale, 32, s_noise=noise)
+        assert (np.abs(On - O) <= allow * (1 + 1e-9) + 1e-13).all()
+        assert (np.abs(On - Oe) <= bound * (1 + 1e-9) + 1e-13).all()
+        moved = max(moved, float(np.abs(On - O).max()))
+    assert moved > 0
+    if s_err == 2.0 ** -13:
+        # at the bound the tests use, the allowance is far below the size of O
+        assert allow.max() < 0.05 * np.abs(O).max()
 
 
 def test_flops_count():
