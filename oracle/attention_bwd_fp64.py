@@ -61,6 +61,70 @@ def attention_bwd_ref(q, k, v, do, causal: bool, scale: float):
     return dQ, dK, dV
 
 
+def attention_bwd_sampled(q, k, v, do, causal: bool, scale: float, qrows, krows,
+                          chunk: int = 1024):
+    """The same gradients for a sample, one (b, h) slice: q, do [Lq, d], k, v
+    [Lk, d].  Returns dQ for the query rows qrows and dK, dV for the key rows
+    krows, in fp64.
+
+    Written out from the same definition for large L: every row's softmax
+    statistics come first (m_i and l_i over all visible keys, chunk by chunk,
+    so LSE_i = m_i + ln l_i), then Delta_i = sum_j P_ij dP_ij for every row;
+    then for a sampled query row i, dS_i. = P_i. (dP_i. - Delta_i) over all
+    keys, dQ_i = scale dS_i. K, and for a sampled key j, over all queries,
+    dV_j = sum_i P_ij dO_i and dK_j = scale sum_i dS_ij q_i, with P_ij =
+    exp(s_ij - LSE_i)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    Lq, d = q.shape
+    Lk = k.shape[0]
+    scale = float(scale)
+    keys = np.arange(Lk)
+    qrows = np.asarray(qrows, dtype=np.int64)
+    krows = np.asarray(krows, dtype=np.int64)
+
+    def block(i0, i1):
+        rows = np.arange(i0, i1)
+        s = scale * (q[i0:i1] @ k.T)
+        vis = keys[None, :] <= rows[:, None] if causal else np.ones(s.shape, bool)
+        return np.where(vis, s, -np.inf), vis
+
+    lse = np.empty(Lq)
+    delta = np.empty(Lq)
+    for i0 in range(0, Lq, chunk):
+        i1 = min(Lq, i0 + chunk)
+        s, vis = block(i0, i1)
+        m = s.max(axis=1, keepdims=True)
+        e = np.where(vis, np.exp(s - m), 0.0)
+        l = e.sum(axis=1, keepdims=True)
+        lse[i0:i1] = (m + np.log(l))[:, 0]
+        p = e / l
+        dp = do[i0:i1] @ v.T
+        delta[i0:i1] = (p * dp).sum(axis=1)
+    dQ = np.empty((len(qrows), d))
+    for n, i in enumerate(qrows):
+        s, vis = block(i, i + 1)
+        p = np.where(vis, np.exp(s - lse[i]), 0.0)[0]
+        dp = v @ do[i]
+        dQ[n] = scale * ((p * (dp - delta[i])) @ k)
+    dK = np.zeros((len(krows), d))
+    dV = np.zeros((len(krows), d))
+    kk, vk = k[krows], v[krows]
+    for i0 in range(0, Lq, chunk):
+        i1 = min(Lq, i0 + chunk)
+        rows = np.arange(i0, i1)
+        s = scale * (q[i0:i1] @ kk.T)
+        vis = krows[None, :] <= rows[:, None] if causal else np.ones(s.shape, bool)
+        p = np.where(vis, np.exp(s - lse[i0:i1, None]), 0.0)
+        dp = do[i0:i1] @ vk.T
+        ds = p * (dp - delta[i0:i1, None])
+        dV += p.T @ do[i0:i1]
+        dK += scale * (ds.T @ q[i0:i1])
+    return dQ, dK, dV
+
+
 def delta_ref(o, do):
     """Delta_i = sum_d dO_id O_id (section 6.2's preprocess quantity)."""
     return (np.asarray(o, dtype=np.float64) * np.asarray(do, dtype=np.float64)).sum(axis=-1)
@@ -76,4 +140,4 @@ def backward_flops(Lq: int, Lk: int, d: int, causal: bool) -> float:
     return float(10.0 * d * vis.sum())
 
 
-__all__ = ["attention_bwd_ref", "delta_ref", "backward_flops"]
+__all__ = ["attention_bwd_ref", "attention_bwd_sampled", "delta_ref", "backward_flops"]

@@ -10,7 +10,8 @@ import pytest
 
 import oracle.attention_bwd_fp64 as bwd_mod
 from oracle import attention_ref
-from oracle.attention_bwd_fp64 import attention_bwd_ref, backward_flops, delta_ref
+from oracle.attention_bwd_fp64 import (attention_bwd_ref, attention_bwd_sampled,
+                                       backward_flops, delta_ref)
 from tests.oracle_pin_checks import rng_qkv
 
 
@@ -68,6 +69,32 @@ def test_torch_autograd(causal, B, H, Lq, Lk, d):
     got = attention_bwd_ref(q, k, v, do, causal, scale)
     for g, t, name in zip(got, (tq, tk, tv), ("dQ", "dK", "dV")):
         np.testing.assert_allclose(g, t.grad.numpy(), rtol=0, atol=1e-12, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lk,chunk", [(90, 90, 16), (70, 130, 1000), (130, 70, 7)])
+def test_sampled_gradients_match_torch_autograd(causal, Lq, Lk, chunk):
+    """The sampled form (for large L) against torch's fp64 autograd of
+    scaled_dot_product_attention on a whole head, rows chosen at the edges
+    and at random."""
+    import torch
+    import torch.nn.functional as F
+    q, k, v = rng_qkv(52, 1, 1, Lq, Lk, 16)
+    do = rng_do(52, q.shape)
+    scale = 0.3
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    mask = None
+    if causal:
+        mask = torch.from_numpy(np.arange(Lk)[None, :] <= np.arange(Lq)[:, None])
+    out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    out.backward(torch.from_numpy(do))
+    qrows = np.array([0, 1, Lq // 2, Lq - 1, 17])
+    krows = np.array([0, 5, Lk // 3, Lk - 1])
+    dQ, dK, dV = attention_bwd_sampled(q[0, 0], k[0, 0], v[0, 0], do[0, 0], causal, scale,
+                                       qrows, krows, chunk=chunk)
+    np.testing.assert_allclose(dQ, tq.grad.numpy()[0, 0, qrows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dK, tk.grad.numpy()[0, 0, krows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dV, tv.grad.numpy()[0, 0, krows], rtol=0, atol=1e-12)
 
 
 @pytest.mark.parametrize("causal", [False, True])
