@@ -51,6 +51,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise FABuildError(
             f"{path} is missing: build it with `python -m "
             "exact_io_aware_08_amd.build` (or __graft_entry__.build())")
+    # torch ships its own HIP runtime under the same soname as ROCm's.  If
+    # this library were loaded first it would bring in the system runtime,
+    # torch would then run on that one or on its own, and launches on torch's
+    # streams fail ("invalid device function").  Loading torch first makes
+    # the library bind to the runtime that owns the caller's tensors and
+    # streams.  Without torch (raw device pointers) nothing changes.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     sig = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
