@@ -62,9 +62,12 @@ constexpr float kPShift = 8.0f;   // P is rounded as P * 2^8
 __device__ inline f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
-// four fp32 values -> four E4M3 bytes (round to nearest even), a in the low byte
+// four fp32 values -> four E4M3 bytes (round to nearest even), a in the low
+// byte.  The first conversion keeps the upper half of its destination, which
+// the second overwrites, so a's own register serves as that destination (no
+// move of a zero first).
 __device__ inline int pack4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 __device__ inline float half_max(float x) {
