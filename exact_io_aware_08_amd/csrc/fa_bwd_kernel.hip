@@ -126,13 +126,15 @@ template <int D, int ROWS, int NW> struct TileLane {
             }
     }
     // copy tile rows [r0, r0 + ROWS) of a [n, D] matrix; rows >= n read row
-    // n - 1 (finite values the masks give weight 0)
+    // n - 1 (finite values the masks give weight 0).  The source is a
+    // wave-uniform base plus a 32-bit unsigned byte offset per lane (the
+    // scalar-base form of the copy); `wave` must be wave-uniform.
     __device__ void copy(const uint16_t* base, int r0, int n, uint16_t* dst, int wave) const {
-        const uint16_t* src = base + (size_t)r0 * D;
+        const char* src = reinterpret_cast<const char*>(base + (size_t)r0 * D);
         const int last = n - 1 - r0;
 #pragma unroll
         for (int i = 0; i < T::BPW; ++i) {
-            const int o = cp_ofs[i] + (min(cp_row[i], last) - cp_row[i]) * D;
+            const unsigned o = (unsigned)(cp_ofs[i] + (min(cp_row[i], last) - cp_row[i]) * D) * 2u;
             __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (wave + NW * i) * 512),
                                              16, 0, 0);
         }

@@ -173,14 +173,18 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     // rows at or past Lk read row Lk - 1 (finite values the mask gives
     // weight 0); tile indexes past the last are clamped to it, so every step
     // issues the same copies
+    // (a wave-uniform tile base plus a 32-bit unsigned offset per lane: the
+    // copy takes the scalar-base form; the LDS destination comes from a
+    // scalar copy of the wave index)
+    const int swave = __builtin_amdgcn_readfirstlane(wave);
     auto issue = [&](int j, const uint8_t* base, const int (&ofs)[G::BPW], uint8_t* dst) {
         const int kv0 = min(j, nt - 1) * BN;
         const uint8_t* src = base + (size_t)kv0 * D;
         const int last = Lk - 1 - kv0;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i) {
-            const int o = ofs[i] + (min(crow[i], last) - crow[i]) * D;
-            __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (wave + NW * i) * 1024),
+            const unsigned o = (unsigned)(ofs[i] + (min(crow[i], last) - crow[i]) * D);
+            __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (swave + NW * i) * 1024),
                                              16, 0, 0);
         }
     };

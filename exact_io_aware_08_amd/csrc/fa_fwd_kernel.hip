@@ -685,25 +685,30 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // clamp is arithmetic and tile indexes past the last one are clamped to
     // it, so every step issues the same copies without branches and the
     // counted waits below stay exact.
+    // The source is a wave-uniform tile base plus a 32-bit unsigned byte
+    // offset per lane (the copy takes the scalar-base form, with no 64-bit
+    // address arithmetic per lane), and the LDS destination comes from a
+    // scalar copy of the wave index.
+    const int swave = __builtin_amdgcn_readfirstlane(wave);
     auto issue_k = [&](int j, uint16_t* Kd) {
         const int kv0 = min(j, nt - 1) * BN;   // j >= jlo
-        const uint16_t* Kt = Kh + (size_t)kv0 * D;   // wave-uniform tile base
+        const char* Kt = reinterpret_cast<const char*>(Kh + (size_t)kv0 * D);
         const int last = Lk - 1 - kv0;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i) {
-            const int blk = wave + NW * i;
-            const int ko = kofs_g[i] + (min(krow_g[i], last) - krow_g[i]) * D;
+            const int blk = swave + NW * i;
+            const unsigned ko = (unsigned)(kofs_g[i] + (min(krow_g[i], last) - krow_g[i]) * D) * 2u;
             __builtin_amdgcn_global_load_lds(Kt + ko, (FA_LDS void*)(Kd + blk * 512), 16, 0, 0);
         }
     };
     auto issue_v = [&](int j, uint16_t* Vd) {
         const int kv0 = min(j, nt - 1) * BN;
-        const uint16_t* Vt = Vh + (size_t)kv0 * D;
+        const char* Vt = reinterpret_cast<const char*>(Vh + (size_t)kv0 * D);
         const int last = Lk - 1 - kv0;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i) {
-            const int blk = wave + NW * i;
-            const int vo = vofs_g[i] + (min(vrow_g[i], last) - vrow_g[i]) * D;
+            const int blk = swave + NW * i;
+            const unsigned vo = (unsigned)(vofs_g[i] + (min(vrow_g[i], last) - vrow_g[i]) * D) * 2u;
             __builtin_amdgcn_global_load_lds(Vt + vo, (FA_LDS void*)(Vd + blk * 512), 16, 0, 0);
         }
     };
