@@ -74,8 +74,10 @@ def build(isa_dir: str | None = None, verbose: bool = False, csrc: str = CSRC,
         run([base + FILE_FLAGS.get(s, []) + ["-c", os.path.join(csrc, s), "-o", o]
              for s, o in zip(SOURCES, objs)], isa_dir or tmpdir)
         tmp = out + ".tmp"
-        run([[hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]],
-            tmpdir)
+        # -z defs: a kernel whose host pass failed leaves its launch stub
+        # undefined, which must stop the build rather than the first load
+        run([[hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs,
+              "-o", tmp]], tmpdir)
         os.replace(tmp, out)
     return out
 

@@ -66,6 +66,10 @@ template <class T, int N> struct VecOf {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
 constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
+#ifndef FA_LAZY
+#define FA_LAZY 8.0f
+#endif
+constexpr float kLazy = FA_LAZY;   // bf16 direct kernel: reference-max slack (log2 units)
 
 // ---- element traits -------------------------------------------------------
 
@@ -460,8 +464,11 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // bf16 kernel with direct global->LDS tile loads (gfx950).
 //
 // K and V tiles are copied from HBM straight into LDS with
-// global_load_lds_dwordx4 (lane L of a wave instruction lands at byte 16*L
-// of a 1 KB LDS block), so no registers or VALU instructions stage them.
+// buffer_load_dwordx4 ... lds (lane L of a wave instruction lands at byte
+// 16*L of a 1 KB LDS block), so no registers or VALU instructions stage
+// them; with the buffer form the compiler also counts the LDS fragment
+// reads precisely (lgkmcnt(n) instead of lgkmcnt(0)), so they overlap the
+// MFMAs.
 // Both tiles keep their natural row layout [key][d] with the 16-byte chunks
 // of each row XOR-swizzled by a function of the row index (a different one
 // for K and V, chosen so that both fragment reads are free of LDS bank
@@ -471,8 +478,10 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // 16-lane group, lane l receives element l%4 of the 8-byte rows supplied by
 // lanes (l%16)/4 + 4i (i = 0..3), so rows "4 keys x 4 d-quads" give every
 // lane 4 keys of its own d column; two such reads form one operand.
-// Tile rows at or beyond Lk are loaded from row Lk-1 (finite data that the
-// mask turns into weight 0).  The two tile buffers are separate LDS objects
+// Tile rows at or beyond Lk arrive as zeros from the buffer's range check
+// (finite data that the mask turns into weight 0).  The running max that P
+// is taken against moves lazily (only when a tile's max exceeds it by more
+// than 2^8 in P).  The two tile buffers are separate LDS objects
 // and the key loop is unrolled by two, so each access names its buffer.
 // ===========================================================================
 
@@ -541,6 +550,20 @@ template <int D> struct DGeom {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
+// One 16-byte-per-lane copy HBM -> LDS through a raw buffer resource of
+// `bytes` bytes at `base`: lane L's 16 bytes at base + vofs land at byte
+// 16 L of the 1 KB LDS block `dst`; a lane whose range ends past `bytes`
+// gets zeros and touches no memory.  Word 3 of the resource: 32-bit data
+// format, no swizzle or stride (gfx9 family).  The buffer-resource type
+// exists only for the device, so the host pass sees an empty body.
+__device__ inline void buffer_copy16(const void* base, int bytes, unsigned vofs,
+                                     __attribute__((address_space(3))) void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
+                                                     0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, vofs, 0, 0, 0);
+#endif
+}
 
 // Which keys a query sees: all of them, the causal prefix j <= i (top-left),
 // or a sliding window i - wl <= j <= i + wr (the window-size pair of
@@ -668,50 +691,36 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // Per-lane parts of the copy addresses (element offsets inside a tile):
     // LDS block blk of 64 chunks, lane's physical chunk p -> tile row and
     // logical chunk.  K rows are stored in the permuted slot order of k_slot.
-    int kofs_g[G::BPW], vofs_g[G::BPW], krow_g[G::BPW], vrow_g[G::BPW];
+    unsigned kofs_g[G::BPW], vofs_g[G::BPW];   // byte offsets inside a tile
 #pragma unroll
     for (int i = 0; i < G::BPW; ++i) {
         const int blk = wave + NW * i;
         const int p = blk * 64 + lane;
         const int row = p / CPR;
         const int kr = (row & ~31) | (16 * ((row >> 2) & 1) + 4 * ((row & 31) >> 3) + (row & 3));
-        krow_g[i] = kr;
-        vrow_g[i] = row;
-        kofs_g[i] = kr * D + ((p % CPR) ^ G::f_k(row)) * 8;
-        vofs_g[i] = row * D + ((p % CPR) ^ G::f_v(row)) * 8;
+        kofs_g[i] = (unsigned)(kr * D + ((p % CPR) ^ G::f_k(row)) * 8) * 2u;
+        vofs_g[i] = (unsigned)(row * D + ((p % CPR) ^ G::f_v(row)) * 8) * 2u;
     }
-    // Each wave copies BPW 1 KB blocks of a tile; rows at or past Lk read
-    // row Lk-1 instead (finite values that the mask gives weight 0).  The
-    // clamp is arithmetic and tile indexes past the last one are clamped to
-    // it, so every step issues the same copies without branches and the
-    // counted waits below stay exact.
-    // The source is a wave-uniform tile base plus a 32-bit unsigned byte
-    // offset per lane (the copy takes the scalar-base form, with no 64-bit
-    // address arithmetic per lane), and the LDS destination comes from a
-    // scalar copy of the wave index.
+    // Each wave copies BPW 1 KB blocks of a tile through a buffer resource
+    // whose base is the tile's first row and whose size covers only its
+    // rows below Lk (none for a tile index past the block's last one, the
+    // prefetch after the final tile).  A lane whose row lies outside reads
+    // zeros from the hardware's range check without touching memory: finite
+    // values that the mask gives weight 0.  So every step issues the same
+    // copies, the per-lane offsets never change, and the counted waits
+    // below stay exact; the LDS destination comes from a scalar copy of the
+    // wave index.
     const int swave = __builtin_amdgcn_readfirstlane(wave);
-    auto issue_k = [&](int j, uint16_t* Kd) {
-        const int kv0 = min(j, nt - 1) * BN;   // j >= jlo
-        const char* Kt = reinterpret_cast<const char*>(Kh + (size_t)kv0 * D);
-        const int last = Lk - 1 - kv0;
+    auto issue = [&](const uint16_t* Xh, int j, uint16_t* Xd, const unsigned (&ofs)[G::BPW]) {
+        const int jc = min(j, nt - 1);   // j >= jlo
+        const int bytes = j < nt ? min(BN, Lk - jc * BN) * D * 2 : 0;
+        const uint16_t* base = Xh + (size_t)jc * BN * D;
 #pragma unroll
-        for (int i = 0; i < G::BPW; ++i) {
-            const int blk = swave + NW * i;
-            const unsigned ko = (unsigned)(kofs_g[i] + (min(krow_g[i], last) - krow_g[i]) * D) * 2u;
-            __builtin_amdgcn_global_load_lds(Kt + ko, (FA_LDS void*)(Kd + blk * 512), 16, 0, 0);
-        }
+        for (int i = 0; i < G::BPW; ++i)
+            buffer_copy16(base, bytes, ofs[i], (FA_LDS void*)(Xd + (swave + NW * i) * 512));
     };
-    auto issue_v = [&](int j, uint16_t* Vd) {
-        const int kv0 = min(j, nt - 1) * BN;
-        const char* Vt = reinterpret_cast<const char*>(Vh + (size_t)kv0 * D);
-        const int last = Lk - 1 - kv0;
-#pragma unroll
-        for (int i = 0; i < G::BPW; ++i) {
-            const int blk = swave + NW * i;
-            const unsigned vo = (unsigned)(vofs_g[i] + (min(vrow_g[i], last) - vrow_g[i]) * D) * 2u;
-            __builtin_amdgcn_global_load_lds(Vt + vo, (FA_LDS void*)(Vd + blk * 512), 16, 0, 0);
-        }
-    };
+    auto issue_k = [&](int j, uint16_t* Kd) { issue(Kh, j, Kd, kofs_g); };
+    auto issue_v = [&](int j, uint16_t* Vd) { issue(Vh, j, Vd, vofs_g); };
     // K fragment (A operand of S^T) for d-step s of key block mb: slot row
     // mb*32 + col, logical chunk 2s + half; f_k(mb*32 + col) = f_k(col), so
     // mb only adds a whole-row offset and one lane offset per s suffices.
@@ -819,7 +828,13 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         for (int w = 1; w < NMB; w *= 2)
 #pragma unroll
             for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
-        const float m_new = fmaxf(m_run[nb], half_max(pm[0]) * c);
+        // The reference max moves only when the tile's max exceeds it by
+        // more than kLazy (base 2): until then P <= 2^kLazy, which bf16 and
+        // the fp32 sums hold without loss, and O, l and LSE all use the same
+        // reference, so the result is that of the exact update.  On most
+        // tiles no row moves and the O rescale below is skipped.
+        const float m_tile = half_max(pm[0]) * c;
+        const float m_new = (m_tile > m_run[nb] + kLazy) ? m_tile : m_run[nb];
         const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
         alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         // rescale O before the exponentials so that they and the PV MFMAs
