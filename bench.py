@@ -41,6 +41,7 @@ BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                                  "fa_bwd_kernel.hip")
 FP8_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                                  "fa_fp8_kernel.hip")
+SHARED_DEVICE_HEADER = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc", "fa_copy.h")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -49,10 +50,11 @@ def log(msg):
 
 
 def kernel_source_hash(path: str = None) -> str:
-    """Hash of a kernel source (default: the forward's) with comments and
+    """Hash of a kernel source (default: the forward's) and the device
+    header every kernel source includes (fa_copy.h), with comments and
     whitespace removed, so that counters stay attached to the code they
     were taken on and survive edits that cannot change it."""
-    text = open(path or KERNEL_SOURCE).read()
+    text = open(path or KERNEL_SOURCE).read() + open(SHARED_DEVICE_HEADER).read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = re.sub(r"\s+", "", text)

@@ -18,8 +18,9 @@
 //    accumulation; P and dS are rounded to bf16 for their second product;
 //  * the resident operands (K and V fragments, or Q and dO fragments) stay
 //    in registers as MFMA B operands for the whole loop;
-//  * streamed tiles (Q and dO, or K and V) are copied HBM -> LDS with
-//    global_load_lds (no registers), rows in natural order, the 16-byte
+//  * streamed tiles (Q and dO, or K and V) are copied HBM -> LDS without
+//    registers (global_load_lds in the dK/dV pass, buffer_load ... lds in
+//    the dQ pass), rows in natural order, the 16-byte
 //    chunks of row r XOR-swizzled by a rotation f(r) of its low bits; the
 //    same tile serves row fragments (ds_read_b128, contraction over d) and
 //    transposed fragments (two ds_read_b64_tr_b16, contraction over rows),
@@ -35,6 +36,7 @@
 
 #include <type_traits>
 
+#include "fa_copy.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -97,8 +99,8 @@ template <int D, int ROWS, int NW> struct TileLane {
     using T = Tile<D, ROWS, NW>;
     static constexpr int NS = D / 16, NDB = D / 32;
     static constexpr int NTL = NDB < 4 ? NDB : 4;
-    int cp_ofs[T::BPW];   // copy: global element offset of this lane's chunk
-    int cp_row[T::BPW];   // copy: its tile row
+    unsigned cp_ofs[T::BPW];   // copy: byte offset of this lane's chunk in the tile
+    int cp_row[T::BPW];        // copy: its tile row
     int rfo[NS];          // row fragment of step s (add blk * 32 * D)
     int tlane[2][NTL];    // transposed fragment, read w, d-block db & 3
 
@@ -108,8 +110,8 @@ template <int D, int ROWS, int NW> struct TileLane {
         for (int i = 0; i < T::BPW; ++i) {
             const int p = (wave + NW * i) * 64 + lane;
             const int row = p / T::CPR;
+            cp_ofs[i] = (unsigned)(row * D + ((p % T::CPR) ^ T::f(row)) * 8) * 2u;
             cp_row[i] = row;
-            cp_ofs[i] = row * D + ((p % T::CPR) ^ T::f(row)) * 8;
         }
 #pragma unroll
         for (int s = 0; s < NS; ++s) rfo[s] = col * D + (((2 * s + h) ^ T::f(col)) * 8);
@@ -125,18 +127,33 @@ template <int D, int ROWS, int NW> struct TileLane {
                 tlane[w][x] = lrow * D + (lc ^ T::f(8 * w + lrow)) * 8 + (vq & 1) * 4;
             }
     }
-    // copy tile rows [r0, r0 + ROWS) of a [n, D] matrix; rows >= n read row
-    // n - 1 (finite values the masks give weight 0).  The source is a
-    // wave-uniform base plus a 32-bit unsigned byte offset per lane (the
-    // scalar-base form of the copy); `wave` must be wave-uniform.
+    // copy tile rows [r0, r0 + ROWS) of a [n, D] matrix.  BUF: through a
+    // buffer resource that covers only rows below n, so rows >= n read
+    // zeros without touching memory; else with global_load_lds from a
+    // wave-uniform base plus a 32-bit lane offset, rows >= n reading row
+    // n - 1.  Either way the values are finite and the masks give them
+    // weight 0.  (The dK/dV pass keeps the second form: its hand-placed
+    // schedule measured 3 % slower with the first; the dQ pass takes the
+    // first, which needs no per-tile lane arithmetic.)  `wave` must be
+    // wave-uniform.
+    template <bool BUF>
     __device__ void copy(const uint16_t* base, int r0, int n, uint16_t* dst, int wave) const {
-        const char* src = reinterpret_cast<const char*>(base + (size_t)r0 * D);
-        const int last = n - 1 - r0;
+        if constexpr (BUF) {
+            const int bytes = max(0, min(ROWS, n - r0)) * D * 2;
 #pragma unroll
-        for (int i = 0; i < T::BPW; ++i) {
-            const unsigned o = (unsigned)(cp_ofs[i] + (min(cp_row[i], last) - cp_row[i]) * D) * 2u;
-            __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (wave + NW * i) * 512),
-                                             16, 0, 0);
+            for (int i = 0; i < T::BPW; ++i)
+                buffer_copy<16>(base + (size_t)r0 * D, bytes, cp_ofs[i],
+                                (FA_LDS void*)(dst + (wave + NW * i) * 512));
+        } else {
+            const char* src = reinterpret_cast<const char*>(base + (size_t)r0 * D);
+            const int last = n - 1 - r0;
+#pragma unroll
+            for (int i = 0; i < T::BPW; ++i) {
+                const unsigned o =
+                    cp_ofs[i] + (unsigned)((min(cp_row[i], last) - cp_row[i]) * D * 2);
+                __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (wave + NW * i) * 512),
+                                                 16, 0, 0);
+            }
         }
     }
     __device__ bf16x8 row_frag(const uint16_t* t, int blk, int s) const {
@@ -284,8 +301,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // copy query tile jt (Q, dO rows and their statistics); wave 0 copies
     // the -LSE / scale values, wave 1 the -Delta values
     auto copy_tile = [&](int jt, uint16_t* Qd, uint16_t* Od, float* Sd) {
-        ln.copy(Qh, jt * BQ, Lq, Qd, wave);
-        ln.copy(Oh, jt * BQ, Lq, Od, wave);
+        ln.template copy<false>(Qh, jt * BQ, Lq, Qd, wave);
+        ln.template copy<false>(Oh, jt * BQ, Lq, Od, wave);
         if (wave < 2) {
             const float* src = (wave == 0 ? nlseh : ndelh) + min(jt * BQ + lane, Lq - 1);
             __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(Sd + wave * BQ), 4, 0, 0);
@@ -517,8 +534,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
 
     auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
         if (j + 1 < nt) {
-            ln.copy(Kh, (j + 1) * BK, Lk, Kn, wave);
-            ln.copy(Vh, (j + 1) * BK, Lk, Vn, wave);
+            ln.template copy<true>(Kh, (j + 1) * BK, Lk, Kn, wave);
+            ln.template copy<true>(Vh, (j + 1) * BK, Lk, Vn, wave);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -557,8 +574,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
         }
         sync_tiles();
     };
-    ln.copy(Kh, 0, Lk, Kb0, wave);
-    ln.copy(Vh, 0, Lk, Vb0, wave);
+    ln.template copy<true>(Kh, 0, Lk, Kb0, wave);
+    ln.template copy<true>(Vh, 0, Lk, Vb0, wave);
     sync_tiles();
     for (int j = 0; j < nt; j += 2) {
         step(j, Kb0, Vb0, Kb1, Vb1);

@@ -29,8 +29,8 @@
 //    j receives byte j % 8 of the 8-byte pieces addressed by lanes 2 i + j / 8
 //    (i = 0..7), so the addressing lane 2 i + t points at key row (i's key)
 //    and d-bytes 8 t .. 8 t + 7 of its half of the 32-d block;
-//  * K and V tiles are copied HBM -> LDS with global_load_lds (16 bytes per
-//    lane, no registers), rows in natural order, the 16-byte chunks of row r
+//  * K and V tiles are copied HBM -> LDS with buffer_load_dwordx4 ... lds
+//    (16 bytes per lane, no registers), rows in natural order, the 16-byte chunks of row r
 //    XOR-swizzled: K by (r >> 1) & 7 (a 16-lane pass of row reads then hits
 //    16 different bank groups), V by 2 ((r >> 1) & 1 | ((r >> 3) & 1) << 1)
 //    (the 32 8-byte pieces of a 32-lane transposed read cover all 64 banks).
@@ -41,6 +41,7 @@
 
 #include <type_traits>
 
+#include "fa_copy.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -161,32 +162,28 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
 
     // ---- tile copy: HBM -> LDS, 16 bytes per lane, no registers ----------
     // physical 16-byte chunk pc of tile row r holds logical chunk pc ^ f(r)
-    int kofs[G::BPW], vofs[G::BPW], crow[G::BPW];
+    unsigned kofs[G::BPW], vofs[G::BPW];
 #pragma unroll
     for (int i = 0; i < G::BPW; ++i) {
         const int pbyte = (wave + NW * i) * 1024 + 16 * lane;
         const int row = pbyte / D, pch = (pbyte % D) / 16;
-        crow[i] = row;
-        kofs[i] = row * D + (pch ^ G::fk(row)) * 16;
-        vofs[i] = row * D + (pch ^ G::fv(row)) * 16;
+        kofs[i] = (unsigned)(row * D + (pch ^ G::fk(row)) * 16);
+        vofs[i] = (unsigned)(row * D + (pch ^ G::fv(row)) * 16);
     }
-    // rows at or past Lk read row Lk - 1 (finite values the mask gives
-    // weight 0); tile indexes past the last are clamped to it, so every step
-    // issues the same copies
-    // (a wave-uniform tile base plus a 32-bit unsigned offset per lane: the
-    // copy takes the scalar-base form; the LDS destination comes from a
-    // scalar copy of the wave index)
+    // Through a buffer resource per tile that starts at its first row and
+    // covers only its rows below Lk (none for the prefetch after the last
+    // tile): rows outside read zeros (finite values the mask gives weight
+    // 0) without touching memory, so every step issues the same copies with
+    // loop-constant lane offsets; the LDS destination comes from a scalar
+    // copy of the wave index.
     const int swave = __builtin_amdgcn_readfirstlane(wave);
-    auto issue = [&](int j, const uint8_t* base, const int (&ofs)[G::BPW], uint8_t* dst) {
-        const int kv0 = min(j, nt - 1) * BN;
-        const uint8_t* src = base + (size_t)kv0 * D;
-        const int last = Lk - 1 - kv0;
+    auto issue = [&](int j, const uint8_t* base, const unsigned (&ofs)[G::BPW], uint8_t* dst) {
+        const int jc = min(j, nt - 1);
+        const int bytes = j < nt ? min(BN, Lk - jc * BN) * D : 0;
+        const uint8_t* src = base + (size_t)jc * BN * D;
 #pragma unroll
-        for (int i = 0; i < G::BPW; ++i) {
-            const unsigned o = (unsigned)(ofs[i] + (min(crow[i], last) - crow[i]) * D);
-            __builtin_amdgcn_global_load_lds(src + o, (FA_LDS void*)(dst + (swave + NW * i) * 1024),
-                                             16, 0, 0);
-        }
+        for (int i = 0; i < G::BPW; ++i)
+            buffer_copy<16>(src, bytes, ofs[i], (FA_LDS void*)(dst + (swave + NW * i) * 1024));
     };
 
     // K fragment (A operand of S^T) for key block mb, d step s: row 32 mb +

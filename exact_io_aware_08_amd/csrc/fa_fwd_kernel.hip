@@ -20,7 +20,7 @@
 //    straddle it are masked element-wise (same page, section 4).
 //
 // Two kernels share that method.  fa_fwd_direct_kernel serves bf16: K and V
-// tiles go from HBM straight into LDS (global_load_lds, no registers), and
+// tiles go from HBM straight into LDS (buffer_load ... lds, no registers), and
 // the V^T operand is read with the transposing ds_read_b64_tr_b16.
 // fa_fwd_kernel serves fp32: tiles are staged through registers and V is
 // written to LDS transposed.
@@ -48,6 +48,7 @@
 
 #include <type_traits>
 
+#include "fa_copy.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -550,20 +551,6 @@ template <int D> struct DGeom {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
-// One 16-byte-per-lane copy HBM -> LDS through a raw buffer resource of
-// `bytes` bytes at `base`: lane L's 16 bytes at base + vofs land at byte
-// 16 L of the 1 KB LDS block `dst`; a lane whose range ends past `bytes`
-// gets zeros and touches no memory.  Word 3 of the resource: 32-bit data
-// format, no swizzle or stride (gfx9 family).  The buffer-resource type
-// exists only for the device, so the host pass sees an empty body.
-__device__ inline void buffer_copy16(const void* base, int bytes, unsigned vofs,
-                                     __attribute__((address_space(3))) void* dst) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes,
-                                                     0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, vofs, 0, 0, 0);
-#endif
-}
 
 // Which keys a query sees: all of them, the causal prefix j <= i (top-left),
 // or a sliding window i - wl <= j <= i + wr (the window-size pair of
@@ -717,7 +704,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const uint16_t* base = Xh + (size_t)jc * BN * D;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i)
-            buffer_copy16(base, bytes, ofs[i], (FA_LDS void*)(Xd + (swave + NW * i) * 512));
+            buffer_copy<16>(base, bytes, ofs[i], (FA_LDS void*)(Xd + (swave + NW * i) * 512));
     };
     auto issue_k = [&](int j, uint16_t* Kd) { issue(Kh, j, Kd, kofs_g); };
     auto issue_v = [&](int j, uint16_t* Vd) { issue(Vh, j, Vd, vofs_g); };
