@@ -108,6 +108,23 @@ def flops_of(w, causal: bool, window=None) -> float:
     return 4.0 * w.B * w.H * w.d * pairs
 
 
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def compulsory_bytes(w, backward: bool = False, fp8: bool = False) -> float:
+    """Algorithmic HBM bytes of one call: every input read once and every
+    output written once.  Forward: q, k, v in, o and the fp32 LSE out (FP8:
+    one-byte inputs, bf16 o).  Backward: q, k, v, o, dO and LSE in, dq, dk,
+    dv out."""
+    esize = {"bf16": 2, "fp32": 4, "fp8": 1}[w.dtype]
+    nq, nk = w.B * w.H * w.Lq * w.d, w.B * w.H * w.Lk * w.d
+    rows = 4.0 * w.B * w.H * w.Lq
+    if backward:
+        return (3 * nq + 2 * nk) * esize + rows + (nq + 2 * nk) * esize
+    osize = 2 if fp8 else esize
+    return (nq + 2 * nk) * esize + nq * osize + rows
+
+
 def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
                  window=None):
     """Time the oracle on whole (batch, head) slices of the workload, one
@@ -277,6 +294,14 @@ def main(argv=None):
     import exact_io_aware_08_amd as fa
     from seeded_inputs import WORKLOADS, workload_inputs
 
+    props = torch.cuda.get_device_properties(0)
+    sclk = getattr(props, "clock_rate", 0) / 1e3   # kHz -> MHz, where torch reports it
+    cus = props.multi_processor_count
+    log(f"bench: {props.name}: {cus} CUs" + (
+        f", max sclk {sclk:.0f} MHz -> {cus} x 4096 bf16 flops/clk x sclk = "
+        f"{cus * 4096 * sclk * 1e6 / 1e12:.1f} TFLOP/s dense bf16" if sclk else "") +
+        "; the roofline uses the published peaks (bf16 2500, FP8 5000 TFLOP/s, HBM 8 TB/s)")
+
     w = WORKLOADS[a.workload]
     mode = a.mode or w.modes[0]
     causal = mode == "causal" or (mode == "bwd" and "causal" in w.modes)
@@ -401,6 +426,34 @@ def main(argv=None):
         log(f"bench: oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores "
             f"-> {cpu['value'] * 1e3:.2f} GFLOP/s; parity on sample {parity}")
 
+    # the kernel's bound: MFMA unless its arithmetic intensity (algorithmic
+    # flops per compulsory byte) is below the ridge point peak / 8 TB/s
+    cbytes = compulsory_bytes(w, backward, fp8)
+    hbm_bound = flops / cbytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = traffic_from_profiles(w.name, backward, fp8)
+    if hbm_bound:
+        gbs = cbytes / (ms_kernel * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 5), "traffic": traffic}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic}
+    roofline.update({
+        "kernel_ms": round(ms_kernel, 5),
+        "kernel_ms_median": round(float(np.median(per)), 5),
+        "kernel_ms_min": round(float(min(per)), 5),
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": cbytes,
+        "arithmetic_intensity": round(flops / cbytes, 2),
+        # achieved HBM rates: compulsory bytes, and measured bytes (rocprofv3
+        # FETCH_SIZE + WRITE_SIZE of the committed profile) over the mean launch
+        "hbm_gbs_algorithmic": round(cbytes / (ms_kernel * 1e-3) / 1e9, 2),
+        "hbm_gbs_measured": None if traffic is None
+        else round(traffic / (ms_kernel * 1e-3) / 1e9, 2),
+    })
+    if hbm_bound:
+        roofline["tflops_achieved"] = round(achieved, 3)
+
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -421,12 +474,7 @@ def main(argv=None):
                    "num_splits": splits or None, "pass": "backward" if backward else "forward",
                    "scale": w.scale, "seed": w.seed,
                    "sigma_qk": w.sigma_qk, "sigma_v": w.sigma_v},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
-                     "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 5),
-                     "traffic": traffic_from_profiles(w.name, backward, fp8),
-                     "kernel_ms": round(ms_kernel, 5),
-                     "algorithmic_flops_per_launch": flops},
+        "roofline": roofline,
         "cpu_baseline": None if cpu is None else {
             k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
     }

@@ -1,0 +1,54 @@
+"""Host-side arithmetic of bench.py (no GPU): algorithmic flops and bytes
+against the measurement table's figures, the roofline bound each workload
+gets, and the one-GPU guard."""
+import math
+
+import pytest
+
+import bench
+from seeded_inputs import WORKLOADS
+
+
+def test_flops_match_the_formula():
+    # 4 B H Lq Lk d, halved for causal: 1.0995e12 for the 16K causal workload
+    w = WORKLOADS["bf16_causal_16k_d128"]
+    assert bench.flops_of(w, True) == 4.0 * 16 * 16384 * 16384 * 128 / 2
+    assert math.isclose(bench.flops_of(w, True), 1.0995e12, rel_tol=1e-4)
+    w = WORKLOADS["bf16_4k_d128"]
+    assert bench.flops_of(w, False) == 2 * bench.flops_of(w, True)
+
+
+@pytest.mark.parametrize("name,mb", [("bf16_causal_1k_d64", 33.8), ("bf16_4k_d128", 269.5),
+                                     ("bf16_causal_16k_d128", 269.5),
+                                     ("bf16_peaky_d256_ragged", 132.9)])
+def test_compulsory_bytes(name, mb):
+    # (2 B H Lq d + 2 B H Lk d) esize + 4 B H Lq
+    w = WORKLOADS[name]
+    want = (2 * w.B * w.H * w.Lq * w.d + 2 * w.B * w.H * w.Lk * w.d) * 2 + 4 * w.B * w.H * w.Lq
+    assert bench.compulsory_bytes(w) == want
+    assert round(want / 1e6, 1) == mb
+
+
+def test_compulsory_bytes_fp8_and_backward():
+    w = WORKLOADS["fp8_causal_16k_d128"]
+    n = w.B * w.H * w.Lq * w.d
+    # one-byte q, k, v in; bf16 o and fp32 LSE out
+    assert bench.compulsory_bytes(w, fp8=True) == 3 * n + 2 * n + 4 * w.B * w.H * w.Lq
+    w = WORKLOADS["bf16_causal_16k_d128"]
+    # q, k, v, o, dO, LSE in; dq, dk, dv out
+    assert bench.compulsory_bytes(w, backward=True) == 8 * n * 2 + 4 * w.B * w.H * w.Lq
+
+
+def test_bound_by_intensity():
+    # ridge = 2500 TFLOP/s / 8 TB/s = 312.5 flop/B: the 1K d=64 causal
+    # workload (254 flop/B) is HBM-side, the others MFMA-side
+    ridge = bench.PEAK_TFLOPS["bf16"] * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    w = WORKLOADS["bf16_causal_1k_d64"]
+    assert bench.flops_of(w, True) / bench.compulsory_bytes(w) < ridge
+    w = WORKLOADS["bf16_causal_16k_d128"]
+    assert bench.flops_of(w, True) / bench.compulsory_bytes(w) > ridge
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
