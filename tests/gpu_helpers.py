@@ -107,16 +107,3 @@ def check_parity(O, LSE, O_ref, LSE_ref, dtype: str, label: str = ""):
     assert ro <= F32_REL, f"{label}: O rel error {ro}"
     assert rl <= F32_REL, f"{label}: LSE rel error {rl}"
     return ro, rl
-
-
-def sample_rows(Lq: int, bm: int, n_random: int, seed: int):
-    """Query rows to check at full size: the edges, every block boundary
-    within the first and last blocks, and random rows."""
-    fixed = {0, 1, 2, 31, 32, 33, 63, 64, Lq - 1, Lq - 2, Lq - 33}
-    for b in (bm - 1, bm, bm + 1, Lq - bm, Lq - bm - 1):
-        fixed.add(b)
-    last_block = (Lq - 1) // bm * bm
-    fixed.update({last_block, last_block + 1})
-    rng = np.random.default_rng(seed)
-    fixed.update(rng.integers(0, Lq, n_random).tolist())
-    return np.array(sorted(r for r in fixed if 0 <= r < Lq))
