@@ -148,3 +148,17 @@ def test_model_detects_conflicts_of_a_single_swizzle():
     same = lambda D, r: r & 15
     assert bank_cycles(v_addresses(128, 0, 0, 0, 0, f=same), 8, 32) == 8
     assert bank_cycles(k_addresses(64, 0, 0, f=lambda D, r: r & 7), 16, 16) == 8
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_k_fragment_offsets_repeat_every_8_steps(D):
+    """The kernel keeps one K-fragment lane offset per d step only for the
+    first 8 steps: the swizzle touches the low 4 bits of the chunk index
+    2s + half, so step s + 8 reads 16 chunks (128 elements) further."""
+    ns = D // 16
+    for lane in range(64):
+        col, half = lane & 31, lane >> 5
+        for st in range(ns):
+            want = col * D + ((2 * st + half) ^ f_k(D, col)) * 8
+            got = col * D + ((2 * (st % 8) + half) ^ f_k(D, col)) * 8 + (st // 8) * 128
+            assert got == want, (D, lane, st)
