@@ -75,11 +75,14 @@ def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = Fal
         if not t or not h3 or h3.group(1) != kernel_source_hash(FP8_KERNEL_SOURCE):
             return None
         return float(t.group(1))
-    h = re.search(r"(?<![a-z0-9_])kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if backward:
+        # the counters cover the backward's own kernels only (the forward
+        # that supplies O and LSE runs outside the timed region)
         h2 = re.search(r"bwd_kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-        if not h2 or h2.group(1) != kernel_source_hash(BWD_KERNEL_SOURCE):
+        if not t or not h2 or h2.group(1) != kernel_source_hash(BWD_KERNEL_SOURCE):
             return None
+        return float(t.group(1))
+    h = re.search(r"(?<![a-z0-9_])kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     if not h or not t or h.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))

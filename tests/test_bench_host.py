@@ -52,3 +52,33 @@ def test_bound_by_intensity():
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def _profile(tmp_path, name, fwd, bwd, fp8, nbytes=1.5e8):
+    (tmp_path / name).write_text(
+        f"# kernel_source_sha256_16: {fwd}\n# bwd_kernel_source_sha256_16: {bwd}\n"
+        f"# fp8_kernel_source_sha256_16: {fp8}\nhbm_bytes_per_launch: {nbytes:.6e}\n")
+
+
+def test_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
+    """Committed counters count only while the hash of the kernel they were
+    taken on matches the source; the backward's own hash alone decides for
+    the backward, the FP8 kernel's for FP8."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    fwd = bench.kernel_source_hash()
+    bwd = bench.kernel_source_hash(bench.BWD_KERNEL_SOURCE)
+    fp8 = bench.kernel_source_hash(bench.FP8_KERNEL_SOURCE)
+    stale = "0" * 16
+    _profile(tmp_path, "fa_fwd_w_hbm_counters.txt", fwd, stale, stale)
+    assert bench.traffic_from_profiles("w") == 1.5e8
+    _profile(tmp_path, "fa_fwd_w_hbm_counters.txt", stale, bwd, fp8)
+    assert bench.traffic_from_profiles("w") is None
+    _profile(tmp_path, "fa_bwd_w_hbm_counters.txt", stale, bwd, stale)
+    assert bench.traffic_from_profiles("w", backward=True) == 1.5e8
+    _profile(tmp_path, "fa_bwd_w_hbm_counters.txt", fwd, stale, fp8)
+    assert bench.traffic_from_profiles("w", backward=True) is None
+    _profile(tmp_path, "fa_fwd_w8_hbm_counters.txt", stale, stale, fp8)
+    assert bench.traffic_from_profiles("w8", fp8=True) == 1.5e8
+    _profile(tmp_path, "fa_fwd_w8_hbm_counters.txt", fwd, bwd, stale)
+    assert bench.traffic_from_profiles("w8", fp8=True) is None
+    assert bench.traffic_from_profiles("absent") is None
