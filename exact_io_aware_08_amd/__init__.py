@@ -25,7 +25,7 @@ STATUS_NAMES = {
 }
 # every function the C header declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_splitkv",
-           "fa_splitkv_workspace_size", "fa_bwd", "fa_bwd_workspace_size",
+           "fa_splitkv_workspace_size", "fa_splitkv_suggest", "fa_bwd", "fa_bwd_workspace_size",
            "fa_status_string", "fa_abi_version", "fa_tile_config")
 
 
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitkv.restype = i
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
+    lib.fa_splitkv_suggest.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_splitkv_suggest.restype = i
     lib.fa_bwd.argtypes = [vp] * 9 + [i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
@@ -189,6 +191,13 @@ def splitkv_workspace_size(B, H, Lq, d, num_splits) -> int:
                                                          int(d), int(num_splits)))
 
 
+def splitkv_suggest(B, H, Lq, Lk, d, causal=False, num_cus=0) -> int:
+    """num_splits the library suggests for fa_fwd_splitkv on this shape
+    (``fa_splitkv_suggest``; 1: no split needed, 0: invalid arguments)."""
+    return int(load_library().fa_splitkv_suggest(int(B), int(H), int(Lq), int(Lk), int(d),
+                                                 int(causal), int(num_cus)))
+
+
 def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, num_splits,
                    workspace, workspace_bytes, stream=None):
     """bf16 key-split forward through the C ABI (``fa_fwd_splitkv``):
@@ -272,8 +281,9 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
     return o, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_window", "fa_fwd_splitkv",
-           "splitkv_workspace_size", "fa_bwd", "bwd_workspace_size", "attention",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_splitkv",
+           "splitkv_workspace_size", "splitkv_suggest", "fa_bwd", "bwd_workspace_size",
+           "attention",
            "status_string",
            "abi_version", "tile_config", "load_library", "FAError",
            "FABuildError", "EXPORTS", "LIB_PATH"]

@@ -284,6 +284,27 @@ const char* fa_status_string(int status) {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
+int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_cus) {
+    if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || (causal != 0 && causal != 1)) return 0;
+    fa::TileConfig tc;
+    if (!fa::tile_config(fa::DType::BF16, d, &tc)) return 0;
+    if (num_cus <= 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess || num_cus <= 0)
+            return 0;
+    }
+    const long long base = (long long)B * H * (((long long)Lq + tc.block_m - 1) / tc.block_m);
+    if (base >= num_cus) return 1;
+    // key tiles of the longest query block (causal: it sees min(Lk, Lq) keys)
+    const long long keys = causal ? std::min<long long>(Lk, Lq) : Lk;
+    const long long tiles = (keys + tc.block_n - 1) / tc.block_n;
+    long long splits = (num_cus + base - 1) / base;
+    splits = std::min<long long>(splits, std::max<long long>(1, tiles / 8));
+    return (int)std::min<long long>(splits, kMaxSplits);
+}
+
 int fa_tile_config(int dtype, int d, int* block_m, int* block_n, int* threads) {
     if (dtype < 0 || dtype > 2) return FA_ERR_ARG;
     fa::TileConfig tc;

@@ -49,8 +49,8 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd;
-                              5: fa_fwd_fp8 */
+#define FA_ABI_VERSION 6   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd;
+                              5: fa_fwd_fp8; 6: fa_splitkv_suggest */
 
 enum fa_status {
     FA_OK = 0,
@@ -137,6 +137,15 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 /* Workspace bytes fa_fwd_splitkv needs, or 0 for invalid arguments
  * (B, H, Lq < 1, d not 64/128/256, num_splits outside 1 .. 64).  Host-only. */
 size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits);
+
+/* A num_splits for fa_fwd_splitkv on this shape: 1 when the unsplit grid
+ * (B * H query blocks) already gives every compute unit a workgroup,
+ * else enough splits that the (query block, split) workgroups cover
+ * `num_cus` compute units, with at least 8 key tiles per split and at
+ * most 64 splits.  num_cus <= 0 reads the current device's count.  Returns
+ * 0 for invalid arguments (as fa_fwd's shape checks) or when the device
+ * cannot be queried.  Host-only; no GPU work. */
+int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_cus);
 
 /*
  * bf16 backward: the gradients dq, dk, dv of sum(dout * o) for the forward

@@ -224,3 +224,23 @@ def test_fp8_validation_errors():
     # o is bf16 (2 bytes per element) over 1-byte inputs: o = [Q, Q + 2 |q|)
     assert _st_fp8(k=Q + 2 * 2 * 128 * 128 - 16, o=Q, q=O) == 6
     assert _st_fp8(lse=V + 2 * 128 * 128 - 16) == 6
+
+
+@pytest.mark.parametrize("shape,want", [
+    ((1, 16, 512, 65536, 128, 0), 8),      # 32 query blocks: 8 splits cover 256 CUs
+    ((1, 8, 256, 32768, 128, 0), 32),
+    ((2, 16, 1024, 16384, 128, 0), 2),
+    ((1, 4, 64, 131072, 64, 0), 64),       # capped at 64
+    ((1, 2, 512, 8000, 256, 0), 31),       # capped at 8 tiles per split (250 tiles of 32)
+    ((1, 4, 4096, 4096, 128, 1), 4),       # causal: the longest block's 32 tiles
+    ((4, 16, 2048, 8192, 128, 0), 1),      # 512 query blocks already fill 256 CUs
+    ((1, 1, 100, 100, 128, 0), 1),         # too few tiles to split
+])
+def test_splitkv_suggest(shape, want):
+    assert fa.splitkv_suggest(*shape, num_cus=256) == want
+
+
+def test_splitkv_suggest_invalid():
+    assert fa.splitkv_suggest(0, 1, 8, 8, 128, 0, 256) == 0
+    assert fa.splitkv_suggest(1, 1, 8, 8, 96, 0, 256) == 0
+    assert fa.splitkv_suggest(1, 1, 8, 8, 128, 2, 256) == 0

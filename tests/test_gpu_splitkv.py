@@ -121,3 +121,19 @@ def test_longkv_workload_full():
     O, LSE, _, _ = run_split(q, k, v, False, w.scale, w.splits)
     O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), False, w.scale)
     check_parity(O, LSE, O_ref, L_ref, "bf16", w.name)
+
+
+def test_suggested_split_on_this_device():
+    """fa_splitkv_suggest with the device's own CU count (num_cus = 0), then
+    fa_fwd_splitkv with that many splits, against the oracle."""
+    import torch
+    B, H, Lq, Lk, d = 1, 2, 200, 6000, 128
+    n = fa.splitkv_suggest(B, H, Lq, Lk, d, False)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"suggested splits {n} for {cus} CUs")
+    assert n == fa.splitkv_suggest(B, H, Lq, Lk, d, False, cus) and 1 < n <= 64
+    q, k, v = make_inputs(44, B, H, Lq, Lk, d, "bf16")
+    s = f32_scale(d)
+    O, L, _, _ = run_split(q, k, v, False, s, n)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), False, s)
+    check_parity(O, L, O_ref, L_ref, "bf16", f"suggested {n} splits")
