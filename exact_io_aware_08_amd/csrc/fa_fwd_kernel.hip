@@ -67,6 +67,7 @@ template <class T, int N> struct VecOf {
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
 constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
+constexpr float kLazy = 8.0f;   // bf16 direct kernel: reference-max slack (log2 units)
 
 // ---- element traits -------------------------------------------------------
 
@@ -508,6 +509,9 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 #ifndef FA_DVN
 #define FA_DVN 6
 #endif
+#ifndef FA_LAZYC
+#define FA_LAZYC 1
+#endif
 template <int BN_, int NW_, int WPE_, int NBQ_> struct DCfgT {
     static constexpr int BN = BN_, NW = NW_, WPE = WPE_, NBQ = NBQ_;
 };
@@ -632,13 +636,14 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             qf[nb][s] = (row < Lq) ? E::load(Qh + (size_t)row * D + s * 16 + half * 8) : Frag{};
     }
     f32x16 oacc[NBQ][NDB];
-    float m_run[NBQ], l_run[NBQ];
+    float m_run[NBQ], l_run[NBQ], c_run[NBQ];
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[nb][db] = f32x16{};
         m_run[nb] = -__builtin_inff();
         l_run[nb] = 0.f;
+        c_run[nb] = 0.f;
     }
 
     // key tiles [jlo, nt) hold every key a row of this block may see
@@ -777,7 +782,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     // mask, running max and O rescale for query block nb; returns the max
     // used by the exponentials and sets alpha
-    auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha) {
+    auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha, float& hmax) {
         const int qb0 = q0w + 32 * nb;
         // some key of the tile lies past Lk, right of a row's last key, or
         // (window) left of a row's first key
@@ -818,12 +823,25 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         for (int w = 1; w < NMB; w *= 2)
 #pragma unroll
             for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
+#if FA_LAZYC
+        // The reference max moves only when the tile's max exceeds it by
+        // more than kLazy (base 2), so most tiles skip the O rescale.  P <= 2^8
+        // stays exact in range; but the key at a row's maximum then gets a
+        // rounded bf16 weight 2^delta instead of exp2(0) = 1, while l sums the
+        // unrounded P.  That one mismatch is carried separately (c_run, the
+        // rounding of each lane's tile maximum) and O is normalised by l plus
+        // it, so the global maximum's weight is consistent between numerator
+        // and denominator as with the exact max; LSE keeps the true l.
+        hmax = pm[0];
+        const float m_tile = half_max(pm[0]) * c;
+        const float m_new = (m_tile > m_run[nb] + kLazy) ? m_tile : m_run[nb];
+#else
         // The exact running max: the key that holds a row's maximum gets
         // P = exp2(0) = 1, exact in bf16, so the dominant term of a peaky row
-        // is not rounded (a reference that lags the max, even by less than
-        // 2^8 in P, rounds it and costs up to 2^-9 |v| in O: 0.026 against
-        // 0.016 on the d = 256 peaky workload).
+        // is not rounded.
+        hmax = pm[0];
         const float m_new = fmaxf(m_run[nb], half_max(pm[0]) * c);
+#endif
         const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
         alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         // rescale O before the exponentials so that they and the PV MFMAs
@@ -916,15 +934,23 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             s_tile(Kc, sacc);
             float alpha[NBQ], rs[NBQ];
             Frag pf[NBQ][NMB][2];
+            float dmax[NBQ];
 #pragma unroll
             for (int nb = 0; nb < NBQ; ++nb) {
-                const float m_use = row_max(kv0, nb, sacc[nb], alpha[nb]);
+                float hmax;
+                const float m_use = row_max(kv0, nb, sacc[nb], alpha[nb], hmax);
                 rs[nb] = exps(sacc[nb], m_use, pf[nb]);
+                // bf16 rounding of P at this lane's tile maximum
+                const float pmx = __builtin_amdgcn_exp2f(__builtin_fmaf(hmax, c, -m_use));
+                dmax[nb] = FA_LAZYC ? (float)(__bf16)pmx - pmx : 0.f;
             }
             pv(Vc, pf);
             sched_pv_valu();
 #pragma unroll
-            for (int nb = 0; nb < NBQ; ++nb) l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
+            for (int nb = 0; nb < NBQ; ++nb) {
+                l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
+                if (FA_LAZYC) c_run[nb] = c_run[nb] * alpha[nb] + dmax[nb];
+            }
         }
         sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
     };
@@ -942,10 +968,12 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
         const float lt = half_sum(l_run[nb]);
+        // O is normalised by the sum of the weights its numerator used
+        const float ln = FA_LAZYC ? lt + half_sum(c_run[nb]) : lt;
         // a window or a key split can leave a row with no key: O = 0 and
         // LSE = -inf (log of an empty sum)
         constexpr bool MAY_BE_EMPTY = WINDOW || SPLIT;
-        const float inv = (!MAY_BE_EMPTY || lt > 0.f) ? 1.0f / lt : 0.f;
+        const float inv = (!MAY_BE_EMPTY || lt > 0.f) ? 1.0f / ln : 0.f;
         const int row = q0w + 32 * nb + col;
         if (SPLIT && row < Lq) {
             float* Op = Opart + (((size_t)split * BH + bh) * Lq + row) * D;
