@@ -82,6 +82,33 @@ def test_bf16_causal_1k_workload_full():
     full_case(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, "bf16", True)
 
 
+# ---- a running max that rises slowly along the keys -----------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_every_tile(causal):
+    """Scores rising linearly along the keys, so every tile holds a new row
+    maximum: row i's scores rise by 4 + 8 i / Lq (base 2) in total, so some
+    rows keep the first tile's reference to the end (P up to nearly 2^8)
+    and others move it partway.  K is zero except its first component,
+    j / Lk (bf16), and Q's first component sets the slope; V is Gaussian."""
+    from seeded_inputs import round_to_bf16_bits
+    B, H, Lq, Lk, d = 1, 2, 96, 3000, 128
+    scale = f32_scale(d)
+    c = scale * 1.4426950408889634
+    rng = np.random.default_rng(61)
+    kf = np.zeros((B, H, Lk, d), np.float32)
+    kf[..., 0] = np.arange(Lk, dtype=np.float32) / Lk
+    qf = np.zeros((B, H, Lq, d), np.float32)
+    qf[..., 0] = ((4.0 + 8.0 * np.arange(Lq) / Lq) / c).astype(np.float32)
+    vf = rng.standard_normal((B, H, Lk, d), dtype=np.float32)
+    q, k, v = (round_to_bf16_bits(x) for x in (qf, kf, vf))
+    label = f"rising scores causal={causal}"
+    say(f"case {label}")
+    O, LSE = run_fa(q, k, v, causal, scale)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), causal, scale)
+    check_parity(O, LSE, O_ref, L_ref, "bf16", label)
+
+
 # ---- full-size workloads, every row ---------------------------------------
 
 def full_workload(name, causal):
