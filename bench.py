@@ -112,6 +112,9 @@ def flops_of(w, causal: bool, window=None) -> float:
 
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
+# bound on the FP8 matrix unit's error in S, as a fraction of sum_t |q_t k_t|
+# (eight times the largest seen over 8192 random E4M3 dot products)
+FP8_S_ERR = 2.0 ** -13
 
 
 def compulsory_bytes(w, backward: bool = False, fp8: bool = False) -> float:
@@ -175,14 +178,15 @@ def cpu_baseline_fp8(w, causal, q8, k8, v8, ds, gpu_out, budget_s=15.0, max_head
     host time is spent; report the GPU result's distance to it and to the
     exact definition on that sample."""
     import exact_io_aware_08_amd as fa
-    from oracle import attention_fp8_blocked, attention_ref, default_workers, fp8_flops
+    from oracle import (attention_fp8_blocked, attention_ref, default_workers, fp8_error_bound,
+                        fp8_flops)
     from seeded_inputs import widen, widen_fp8
     block = fa.tile_config("fp8", w.d)[1]
     O_gpu, L_gpu = gpu_out
     slices = [(b, h) for b in range(w.B) for h in range(w.H)]
     if max_heads:
         slices = slices[:max_heads]
-    spent, done, eb, ee, el = 0.0, 0, 0.0, 0.0, 0.0
+    spent, done, eb, ee, el, rb, rx = 0.0, 0, 0.0, 0.0, 0.0, 0.0, 0.0
     for b, h in slices:
         sl = (slice(b, b + 1), slice(h, h + 1))
         qs, ks, vs = (widen_fp8(x[sl], s) for x, s in zip((q8, k8, v8), ds))
@@ -194,10 +198,22 @@ def cpu_baseline_fp8(w, causal, q8, k8, v8, ds, gpu_out, budget_s=15.0, max_head
         eb = max(eb, float(np.abs(og - O_blk).max()))
         el = max(el, float(np.abs(L_gpu[sl].astype(np.float64) - L_blk).max()))
         if done == 1:
+            # sampled rows of the first slice: error against the exact
+            # definition, and the worst ratio of the GPU's error to the FP8
+            # bars (<= 1: within them): vs the blocked algorithm, 2^-8 |O_blk|
+            # + 1e-5 + the allowance for the matrix unit's S error (at most
+            # 2^-13 of sum_t |q_t k_t|); vs the definition, the derived
+            # E4M3 bound + 2^-8 |O| + 1e-4 (bf16 output and fp32 slack)
             rows = np.arange(0, w.Lq, max(1, w.Lq // 256))
             O_ex, _ = attention_ref(qs, ks, vs, causal, w.scale, rows=rows,
                                     workers=default_workers())
-            ee = float(np.abs(og[:, :, rows] - O_ex).max())
+            og_r = og[:, :, rows]
+            ee = float(np.abs(og_r - O_ex).max())
+            Ob_r, _, allow = attention_fp8_blocked(qs, ks, vs, causal, w.scale, block, rows=rows,
+                                                   s_err=FP8_S_ERR)
+            bound = fp8_error_bound(qs, ks, vs, causal, w.scale, rows=rows, s_err=FP8_S_ERR)
+            rb = float((np.abs(og_r - Ob_r) / (2.0 ** -8 * np.abs(Ob_r) + 1e-5 + allow)).max())
+            rx = float((np.abs(og_r - O_ex) / (bound + 2.0 ** -8 * np.abs(O_ex) + 1e-4)).max())
         if spent >= budget_s:
             break
     fl = done * fp8_flops(w.Lq, w.Lk, w.d, causal)
@@ -208,7 +224,9 @@ def cpu_baseline_fp8(w, causal, q8, k8, v8, ds, gpu_out, budget_s=15.0, max_head
                    f"default), {spent:.2f} s wall"),
         "seconds": spent,
     }, {"max_abs_err_O_vs_blocked_fp8": eb, "max_abs_err_LSE": el,
-        "max_abs_err_O_vs_exact_sampled_rows": ee, "slices": done}
+        "max_abs_err_O_vs_exact_sampled_rows": ee,
+        "worst_ratio_to_fp8_bar_vs_blocked_sampled_rows": rb,
+        "worst_ratio_to_fp8_bound_vs_exact_sampled_rows": rx, "slices": done}
 
 
 def cpu_baseline_bwd(w, causal, q, k, v, do, grads, budget_s=15.0, max_heads=None):

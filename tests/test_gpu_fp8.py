@@ -18,6 +18,7 @@ oracle/attention_fp8.py):
   each P that the S error could move across a rounding midpoint plus the
   continuous effect of the S error); and, with O_blk rounded to bf16 like
   the kernel's output, RMS(O - O_blk16) <= 3e-3 RMS(O_blk).
+The full-size workload is checked on every row of two heads.
 """
 import numpy as np
 import pytest
@@ -112,21 +113,20 @@ def test_fp8_2k_causal_all_rows():
     fp8_case(74, 1, 4, 2048, 2048, 128, True)
 
 
-def test_fp8_16k_workload_sampled():
+def test_fp8_16k_workload_two_heads_all_rows():
     """The FP8 bench workload (B=1, H=16, L=16384, d=128, causal) in the
-    bench's launch configuration; sampled rows of two heads against both
-    oracles (first and last rows, tile and workgroup edges, random rows)."""
+    bench's launch configuration; every row of two heads against both
+    oracles, in chunks of rows (each row depends only on its own q row)."""
     w = WORKLOADS["fp8_causal_16k_d128"]
     q8, k8, v8, ds = make_inputs_fp8(w.seed, w.B, w.H, w.Lq, w.Lk, w.d)
     O, L = run_fp8(q8, k8, v8, ds, True, w.scale)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 8191, 8192, w.Lq - 1],
-                                     rng.integers(0, w.Lq, 40)]))
     for h in (0, w.H - 1):
         sl = (slice(0, 1), slice(h, h + 1))
         q, k, v = (widen_fp8(x[sl], s) for x, s in zip((q8, k8, v8), ds))
-        check(O[sl][:, :, rows], L[sl][:, :, rows], q, k, v, True, w.scale,
-              f"fp8 16k head {h}", rows=rows)
+        for r0 in range(0, w.Lq, 4096):
+            rows = np.arange(r0, min(w.Lq, r0 + 4096))
+            check(O[sl][:, :, rows], L[sl][:, :, rows], q, k, v, True, w.scale,
+                  f"fp8 16k head {h} rows {r0}..{rows[-1]}", rows=rows)
 
 
 def test_fp8_scale_tiny_closed_form():
