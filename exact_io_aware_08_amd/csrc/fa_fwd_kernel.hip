@@ -500,6 +500,12 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 #ifndef FA_DCFG_256
 #define FA_DCFG_256 32, 8, 2, 1
 #endif
+// Instruction-schedule knobs (measured; each may be overridden with -D):
+// FA_DPRE K fragments read ahead of their S MFMAs; FA_DV0 VALU instructions
+// (the first exponentials) before the first PV MFMA; FA_DVN VALU
+// instructions beside each later PV MFMA.  FA_LAZYC: lazy reference max
+// with the rounding correction (0: the exact running max).  FA_NO_SCHED
+// drops the schedule hints (same results).
 #ifndef FA_DPRE
 #define FA_DPRE 4
 #endif
