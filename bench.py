@@ -41,7 +41,7 @@ BWD_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                                  "fa_bwd_kernel.hip")
 FP8_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc",
                                  "fa_fp8_kernel.hip")
-SHARED_DEVICE_HEADER = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc", "fa_copy.h")
+SHARED_DEVICE_HEADER = os.path.join(ROOT, "exact_io_aware_08_amd", "csrc", "fa_device.h")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -51,7 +51,7 @@ def log(msg):
 
 def kernel_source_hash(path: str = None) -> str:
     """Hash of a kernel source (default: the forward's) and the device
-    header every kernel source includes (fa_copy.h), with comments and
+    header every kernel source includes (fa_device.h), with comments and
     whitespace removed, so that counters stay attached to the code they
     were taken on and survive edits that cannot change it."""
     text = open(path or KERNEL_SOURCE).read() + open(SHARED_DEVICE_HEADER).read()

@@ -36,7 +36,7 @@
 
 #include <type_traits>
 
-#include "fa_copy.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -256,17 +256,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     // key blocks of a head on one XCD; causal: the first key blocks (seen by
     // the most queries) start first
     int bh, kb;
-    {
-        const int p = blockIdx.x;
-        if ((BH & 7) == 0) {
-            const int own = BH >> 3, slot = p >> 3;
-            bh = (p & 7) + 8 * (slot % own);
-            kb = slot / own;
-        } else {
-            bh = p % BH;
-            kb = p / BH;
-        }
-    }
+    xcd_decode(blockIdx.x, BH, bh, kb);
     const int key0 = kb * kKVKeys;
     const int kw0 = key0 + wave * 32;          // this wave's keys kw0 .. kw0 + 31
     const int key = kw0 + col;                 // this lane's key (accumulator column)
@@ -492,17 +482,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
     const int col = lane & 31, h = lane >> 5;
 
     int bh, lvl;
-    {
-        const int p = blockIdx.x;
-        if ((BH & 7) == 0) {
-            const int own = BH >> 3, slot = p >> 3;
-            bh = (p & 7) + 8 * (slot % own);
-            lvl = slot / own;
-        } else {
-            bh = p % BH;
-            lvl = p / BH;
-        }
-    }
+    xcd_decode(blockIdx.x, BH, bh, lvl);
     const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
     const int q0 = qb * kQRows;
     const int q0w = q0 + wave * 32;

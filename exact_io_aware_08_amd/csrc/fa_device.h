@@ -1,4 +1,5 @@
-// Device-side tile copy shared by the kernel sources (HIP only).
+// Device helpers shared by the kernel sources (HIP only): the HBM -> LDS
+// tile copy and the XCD-aware work decode.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +25,24 @@ __device__ inline void buffer_copy(const void* base, int bytes, unsigned vofs,
     else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, vofs, 0, 0, 0);
 #endif
+}
+
+// Work decode shared by the kernels.  Workgroups are dispatched round-robin
+// over the 8 XCDs, so block p runs on XCD p % 8.  With `units` (heads, or
+// (head, split) pairs) a multiple of 8, every block of a unit goes to one
+// XCD, whose L2 then serves the unit's K/V (or Q/dO) re-reads; `lvl` is
+// the block's index among its unit's blocks in dispatch order.  Otherwise
+// units interleave plainly.
+__device__ inline void xcd_decode(int p, int units, int& unit, int& lvl) {
+    if ((units & 7) == 0) {
+        const int own = units >> 3;   // units per XCD
+        const int slot = p >> 3;
+        unit = (p & 7) + 8 * (slot % own);
+        lvl = slot / own;
+    } else {
+        unit = p % units;
+        lvl = p / units;
+    }
 }
 
 }  // namespace fa

@@ -41,7 +41,7 @@
 
 #include <type_traits>
 
-#include "fa_copy.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -122,17 +122,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict_
     // work decode: every query block of a head on one XCD (block p runs on
     // XCD p % 8), causal: the longest rows first
     int bh, lvl;
-    {
-        const int p = blockIdx.x;
-        if ((BH & 7) == 0) {
-            const int own = BH >> 3, slot = p >> 3;
-            bh = (p & 7) + 8 * (slot % own);
-            lvl = slot / own;
-        } else {
-            bh = p % BH;
-            lvl = p / BH;
-        }
-    }
+    xcd_decode(blockIdx.x, BH, bh, lvl);
     const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
     const int q0 = qb * BM;
     const int q0w = q0 + wave * 32;          // this wave's rows q0w .. q0w + 31

@@ -48,7 +48,7 @@
 
 #include <type_traits>
 
-#include "fa_copy.h"
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
@@ -224,18 +224,7 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 
     // ---- work decode: XCD-grouped heads, heaviest causal blocks first ----
     int bh, lvl;
-    {
-        const int p = blockIdx.x;
-        if ((BH & 7) == 0) {
-            const int own = BH >> 3;          // heads per XCD
-            const int slot = p >> 3;
-            bh = (p & 7) + 8 * (slot % own);
-            lvl = slot / own;
-        } else {
-            bh = p % BH;
-            lvl = p / BH;
-        }
-    }
+    xcd_decode(blockIdx.x, BH, bh, lvl);
     const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
     const int q0 = qb * BM;
     const int q0w = q0 + wave * 32 * NBQ;          // first row of this wave
@@ -607,17 +596,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // With key splits, each (head, split) pair counts as one head here.
     int bh, lvl, split = 0;
     {
-        const int p = blockIdx.x;
-        const int BHS = SPLIT ? BH * nsplit : BH;
-        if ((BHS & 7) == 0) {
-            const int own = BHS >> 3;
-            const int slot = p >> 3;
-            bh = (p & 7) + 8 * (slot % own);
-            lvl = slot / own;
-        } else {
-            bh = p % BHS;
-            lvl = p / BHS;
-        }
+        xcd_decode(blockIdx.x, SPLIT ? BH * nsplit : BH, bh, lvl);
         if (SPLIT) {
             split = bh % nsplit;
             bh /= nsplit;
