@@ -28,8 +28,10 @@
  * are device pointers, 16-byte aligned.
  *
  * Ownership: the caller owns every buffer.  The library never allocates,
- * frees or synchronises; each call enqueues exactly one kernel on `stream`
- * (a hipStream_t; 0 means the null stream) and returns.  o and lse must not
+ * frees or synchronises; each call enqueues its kernels on `stream` (a
+ * hipStream_t; 0 means the null stream) and returns: one kernel for the
+ * forward entry points, two for the key split (partials, then merge), three
+ * for the backward (preprocess, dK/dV, dQ).  o and lse must not
  * overlap q, k, v or each other.  Calls are thread-safe (no global mutable
  * state).
  *
