@@ -473,15 +473,18 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 
 // keys per tile, waves per workgroup, waves per SIMD the registers are
 // sized for, 32-query blocks per wave (each K or V fragment read from LDS
-// feeds that many MFMAs).  d = 64 runs 4 waves (128 query rows per workgroup): on short
-// causal sequences (B=4, H=16, L=1024) twice as many, smaller workgroups
-// balance the triangular grid better (21 us against 26 us with 8 waves).
+// feeds that many MFMAs).  d = 64 runs 64-key tiles and 4-wave workgroups
+// (128 query rows) at four waves per SIMD (126 VGPRs, 32 KB of LDS each):
+// 3.5-6 % faster than 128-key tiles at two waves per SIMD on L = 4096 and
+// 16384, the same on the short causal B=4 H=16 L=1024 workload (20.4 us),
+// where 4-wave workgroups balance the triangular grid better than 8-wave
+// ones (21 us against 26 us).
 // d = 256 takes 32-key tiles so that two waves per SIMD fit the register
 // file (O alone is 128 registers): 8 waves of 32 rows, one softmax beside
 // the other wave's MFMAs, 16 % faster than 64-key tiles at one wave per
 // SIMD on the B=1 H=8 Lq=8000 Lk=8192 workload.
 #ifndef FA_DCFG_64
-#define FA_DCFG_64 128, 4, 2, 1
+#define FA_DCFG_64 64, 4, 4, 1
 #endif
 #ifndef FA_DCFG_128
 #define FA_DCFG_128 128, 8, 2, 1

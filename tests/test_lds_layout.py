@@ -23,7 +23,7 @@ import collections
 
 import pytest
 
-SHAPES = [(64, 128), (128, 128), (128, 64), (256, 64), (256, 32)]
+SHAPES = [(64, 128), (64, 64), (128, 128), (128, 64), (256, 64), (256, 32)]
 
 
 def k_slot_key(r):
