@@ -69,6 +69,16 @@ def test_bf16_small(causal, B, H, Lq, Lk, d):
     full_case(23, B, H, Lq, Lk, d, "bf16", causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lq,Lk", [(64, 64), (65, 63), (129, 127), (1, 129),
+                                   (200, 65), (128, 192)])
+def test_bf16_d64_tile_edges(causal, Lq, Lk):
+    # d = 64 runs 64-key tiles and 128-row workgroups: key counts one
+    # below, at and one above a tile edge, and query counts across a
+    # workgroup edge
+    full_case(26, 2, 3, Lq, Lk, 64, "bf16", causal)
+
+
 def test_bf16_peaky_small():
     # sigma 3 on Q, K: large logits exercise the rescaling and tail masks
     full_case(24, 1, 2, 400, 520, 256, "bf16", False, sigma_qk=3.0)
