@@ -59,7 +59,7 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         !aligned16(lse))
         return FA_ERR_ALIGN;
-    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!std::isfinite(scale) || !(scale >= 0.f)) return FA_ERR_SCALE;
     if (mask_status != FA_OK) return mask_status;   // causal / window / split arguments
     if (mask.nsplit) {
         if (!mask.workspace) return FA_ERR_NULL;
@@ -157,12 +157,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
     if (!fa::fp8_tile_config(d, &tc)) return FA_ERR_UNSUPPORTED_D;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return FA_ERR_ALIGN;
-    for (float x : {scale, q_descale, k_descale, v_descale})
+    if (!std::isfinite(scale) || !(scale >= 0.f)) return FA_ERR_SCALE;
+    for (float x : {q_descale, k_descale, v_descale})
         if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_SCALE;
     // the exponent factor of S: scale * q_descale * k_descale * log2(e)
     const double cd = (double)scale * q_descale * k_descale * 1.4426950408889634;
-    const float c = (float)cd;
-    if (!std::isfinite(c) || !(c > 0.f)) return FA_ERR_SCALE;
+    if (!std::isfinite((float)cd)) return FA_ERR_SCALE;
+    const float c = fa::exp2_factor(cd);
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     const long long bh = (long long)B * H;
     const long long grid = (((long long)Lq + tc.block_m - 1) / tc.block_m) * bh;
@@ -274,7 +275,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "B, H, Lq and Lk must be >= 1 and sizes must fit";
     case FA_ERR_UNSUPPORTED_D: return "head dim d must be 64, 128 or 256";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0 (> 0 for fa_bwd; FP8 descales > 0)";
     case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, 1 <= num_splits <= 64, and outputs and workspace must not overlap inputs";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size";

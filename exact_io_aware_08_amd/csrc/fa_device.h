@@ -1,10 +1,51 @@
-// Device helpers shared by the kernel sources (HIP only): the HBM -> LDS
-// tile copy and the XCD-aware work decode.
+// Device helpers shared by the kernel sources (HIP only): vector types, the
+// exchange between the two 32-lane halves of a wave, the HBM -> LDS tile
+// copy and the XCD-aware work decode.
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
+constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
+
+// Which keys a query sees: all of them, the causal prefix j <= i (top-left),
+// or a sliding window i - wl <= j <= i + wr (the window-size pair of
+// "Flash Attention 原理与实现详解" (tbr8.org), section 6.3 "滑动窗口注意力";
+// (wl, 0) is a causal window).  Always also j < Lk.
+enum Mask : int { kFull = 0, kCausal = 1, kWindow = 2 };
+
+// Lane l and lane l ^ 32 hold the same query column of a 32x32 MFMA
+// accumulator; combine their values.  v_permlane32_swap exchanges the two
+// 32-lane halves without going through the LDS crossbar: each lane receives
+// its partner's value.
+__device__ inline float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
+                 __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                    __builtin_bit_cast(unsigned, x),
+                                                    false, false);
+    return __builtin_bit_cast(float, (unsigned)r[0]) +
+           __builtin_bit_cast(float, (unsigned)r[1]);
+}
 
 // One copy of BYTES (4 or 16) per lane HBM -> LDS through a raw buffer
 // resource of `bytes` bytes at `base`: lane L's BYTES at base + vofs land at

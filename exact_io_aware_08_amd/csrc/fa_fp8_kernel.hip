@@ -47,15 +47,9 @@
 namespace fa {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-#define FA_LDS __attribute__((address_space(3)))
-
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kPShift = 8.0f;   // P is rounded as P * 2^8
 
 // 32x32x64 product of E4M3 operands (format code 0 for A and B, no block
@@ -70,16 +64,6 @@ __device__ inline f32x16 mfma8(i32x8 a, i32x8 b, f32x16 c) {
 __device__ inline int pack4(float a, float b, float c, float d) {
     const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-__device__ inline float half_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x), false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ inline float half_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x), false, false);
-    return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 template <int D> struct F8Geom {

@@ -54,19 +54,11 @@
 namespace fa {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <class T, int N> struct VecOf {
     typedef T type __attribute__((ext_vector_type(N)));
 };
 
-constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
-constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e
 constexpr float kLazy = 8.0f;   // bf16 direct kernel: reference-max slack (log2 units)
 
 // ---- element traits -------------------------------------------------------
@@ -108,35 +100,14 @@ struct F32 {
     }
 };
 
-// ---- per-(dtype, d) tile table -------------------------------------------
+// ---- tile table of the register-staged kernel (fp32) ---------------------
 // NBQ: 32-query blocks per wave; BN: keys per K/V tile; NW: waves per
-// workgroup; WPE: waves per SIMD the register budget is sized for (2 lets
-// one wave's softmax overlap another's MFMAs; each wave then has at most
-// 256 registers, all of them architectural VGPRs).
-
-#ifndef FA_CFG_BF16_64
-#define FA_CFG_BF16_64 1, 128, 8, 2
-#endif
-#ifndef FA_CFG_BF16_128
-#define FA_CFG_BF16_128 1, 128, 8, 2
-#endif
-#ifndef FA_CFG_BF16_256
-#define FA_CFG_BF16_256 1, 64, 4, 1
-#endif
-#ifndef FA_CFG_F32
-#define FA_CFG_F32 1, 32, 4, 1
-#endif
-
+// workgroup; WPE: waves per SIMD the register budget is sized for.
 template <int NBQ_, int BN_, int NW_, int WPE_> struct CfgT {
     static constexpr int NBQ = NBQ_, BN = BN_, NW = NW_, WPE = WPE_;
 };
 template <class E, int D> struct Cfg;
-template <> struct Cfg<BF16, 64>  : CfgT<FA_CFG_BF16_64> {};
-template <> struct Cfg<BF16, 128> : CfgT<FA_CFG_BF16_128> {};
-template <> struct Cfg<BF16, 256> : CfgT<FA_CFG_BF16_256> {};
-template <> struct Cfg<F32, 64>   : CfgT<FA_CFG_F32> {};
-template <> struct Cfg<F32, 128>  : CfgT<FA_CFG_F32> {};
-template <> struct Cfg<F32, 256>  : CfgT<FA_CFG_F32> {};
+template <int D> struct Cfg<F32, D> : CfgT<1, 32, 4, 1> {};
 
 template <class E, int D> struct Geom {
     using T = typename E::T;
@@ -170,23 +141,6 @@ template <class E, int D> struct Geom {
     static_assert(LDS_BYTES * WPE * 4 / NW <= 160 * 1024, "LDS budget");
 };
 
-// Lane l and lane l^32 hold the same query column; combine their values.
-// v_permlane32_swap exchanges the two 32-lane halves without going through
-// the LDS crossbar: each lane receives the value of its partner.
-__device__ inline float half_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x),
-                                                    false, false);
-    return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]),
-                 __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ inline float half_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
-                                                    __builtin_bit_cast(unsigned, x),
-                                                    false, false);
-    return __builtin_bit_cast(float, (unsigned)r[0]) +
-           __builtin_bit_cast(float, (unsigned)r[1]);
-}
 
 // Slot of key k (0..31) inside a 32-row block of the K tile in LDS.  MFMA
 // A-operand row r is read by lane r; its accumulator row r sits in lane
@@ -483,40 +437,17 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // file (O alone is 128 registers): 8 waves of 32 rows, one softmax beside
 // the other wave's MFMAs, 16 % faster than 64-key tiles at one wave per
 // SIMD on the B=1 H=8 Lq=8000 Lk=8192 workload.
-#ifndef FA_DCFG_64
-#define FA_DCFG_64 64, 4, 4, 1
-#endif
-#ifndef FA_DCFG_128
-#define FA_DCFG_128 128, 8, 2, 1
-#endif
-#ifndef FA_DCFG_256
-#define FA_DCFG_256 32, 8, 2, 1
-#endif
-// Instruction-schedule knobs (measured; each may be overridden with -D):
-// FA_DPRE K fragments read ahead of their S MFMAs; FA_DV0 VALU instructions
-// (the first exponentials) before the first PV MFMA; FA_DVN VALU
-// instructions beside each later PV MFMA.  FA_LAZYC: lazy reference max
-// with the rounding correction (0: the exact running max).  FA_NO_SCHED
-// drops the schedule hints (same results).
-#ifndef FA_DPRE
-#define FA_DPRE 4
-#endif
-#ifndef FA_DV0
-#define FA_DV0 48
-#endif
-#ifndef FA_DVN
-#define FA_DVN 6
-#endif
-#ifndef FA_LAZYC
-#define FA_LAZYC 1
-#endif
 template <int BN_, int NW_, int WPE_, int NBQ_> struct DCfgT {
     static constexpr int BN = BN_, NW = NW_, WPE = WPE_, NBQ = NBQ_;
 };
 template <int D> struct DCfg;
-template <> struct DCfg<64>  : DCfgT<FA_DCFG_64> {};
-template <> struct DCfg<128> : DCfgT<FA_DCFG_128> {};
-template <> struct DCfg<256> : DCfgT<FA_DCFG_256> {};
+template <> struct DCfg<64>  : DCfgT<64, 4, 4, 1> {};
+template <> struct DCfg<128> : DCfgT<128, 8, 2, 1> {};
+template <> struct DCfg<256> : DCfgT<32, 8, 2, 1> {};
+// Instruction schedule (measured): K fragments read ahead of their S MFMAs;
+// VALU instructions (the first exponentials) before the first PV MFMA; VALU
+// instructions beside each later PV MFMA.
+constexpr int kPreK = 4, kValuPv0 = 48, kValuPvN = 6;
 
 template <int D> struct DGeom {
     static constexpr int NW = DCfg<D>::NW, NT = 64 * NW, WPE = DCfg<D>::WPE;
@@ -550,14 +481,7 @@ template <int D> struct DGeom {
     static_assert(4 * TILE * 2 * (WPE * 4 / NW > 0 ? WPE * 4 / NW : 1) <= 160 * 1024, "LDS budget");
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define FA_LDS __attribute__((address_space(3)))
 
-// Which keys a query sees: all of them, the causal prefix j <= i (top-left),
-// or a sliding window i - wl <= j <= i + wr (the window-size pair of
-// "Flash Attention 原理与实现详解" (tbr8.org), section 6.3 "滑动窗口注意力";
-// (wl, 0) is a causal window).  Always also j < Lk.
-enum Mask : int { kFull = 0, kCausal = 1, kWindow = 2 };
 
 // SPLIT: the key tiles a query block visits are divided among nsplit
 // workgroups; each writes its partial result over its share, normalised,
@@ -736,7 +660,6 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             const uint16_t* a = Vs + cofs + vlane[db & (G::NVL - 1)];
             u[w] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(FA_LDS void*)a);
         }
-        typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 v8 = __builtin_shufflevector(u[0], u[1], 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(Frag, v8);
     };
@@ -757,8 +680,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
                 for (int nb = 0; nb < NBQ; ++nb) sacc[nb][mb] = E::mfma(a, qf[nb][s], sacc[nb][mb]);
             }
-#ifndef FA_NO_SCHED
-        constexpr int NK = NS * NMB, PRE = FA_DPRE;
+        constexpr int NK = NS * NMB, PRE = kPreK;
         __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
         for (int i = 0; i < NK - PRE; ++i) {
@@ -766,7 +688,6 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, PRE * NBQ, 0);
-#endif
     };
     // mask, running max and O rescale for query block nb; returns the max
     // used by the exponentials and sets alpha
@@ -811,7 +732,6 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         for (int w = 1; w < NMB; w *= 2)
 #pragma unroll
             for (int mb = 0; mb + w < NMB; mb += 2 * w) pm[mb] = fmaxf(pm[mb], pm[mb + w]);
-#if FA_LAZYC
         // The reference max moves only when the tile's max exceeds it by
         // more than kLazy (base 2), so most tiles skip the O rescale.  P <= 2^8
         // stays exact in range; but the key at a row's maximum then gets a
@@ -823,13 +743,6 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         hmax = pm[0];
         const float m_tile = half_max(pm[0]) * c;
         const float m_new = (m_tile > m_run[nb] + kLazy) ? m_tile : m_run[nb];
-#else
-        // The exact running max: the key that holds a row's maximum gets
-        // P = exp2(0) = 1, exact in bf16, so the dominant term of a peaky row
-        // is not rounded.
-        hmax = pm[0];
-        const float m_new = fmaxf(m_run[nb], half_max(pm[0]) * c);
-#endif
         const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
         alpha = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
         // rescale O before the exponentials so that they and the PV MFMAs
@@ -880,17 +793,15 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // exponentials of key block 0 first, then each V^T fragment's MFMAs
     // with its two transposed reads and a share of the remaining VALU work
     auto sched_pv_valu = [&]() {
-#ifndef FA_NO_SCHED
         constexpr int NV = NMB * 2 * NDB;   // V^T fragments per tile
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_DV0 * NBQ, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPv0 * NBQ, 0);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, NBQ, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, FA_DVN * NBQ, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPvN * NBQ, 0);
         }
-#endif
     };
     // Wait until at most N of this wave's tile copies are in flight and its
     // LDS reads are done, then the workgroup barrier.  A copy counts as done
@@ -930,14 +841,14 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 rs[nb] = exps(sacc[nb], m_use, pf[nb]);
                 // bf16 rounding of P at this lane's tile maximum
                 const float pmx = __builtin_amdgcn_exp2f(__builtin_fmaf(hmax, c, -m_use));
-                dmax[nb] = FA_LAZYC ? (float)(__bf16)pmx - pmx : 0.f;
+                dmax[nb] = (float)(__bf16)pmx - pmx;
             }
             pv(Vc, pf);
             sched_pv_valu();
 #pragma unroll
             for (int nb = 0; nb < NBQ; ++nb) {
                 l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
-                if (FA_LAZYC) c_run[nb] = c_run[nb] * alpha[nb] + dmax[nb];
+                c_run[nb] = c_run[nb] * alpha[nb] + dmax[nb];
             }
         }
         sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
@@ -957,7 +868,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     for (int nb = 0; nb < NBQ; ++nb) {
         const float lt = half_sum(l_run[nb]);
         // O is normalised by the sum of the weights its numerator used
-        const float ln = FA_LAZYC ? lt + half_sum(c_run[nb]) : lt;
+        const float ln = lt + half_sum(c_run[nb]);
         // a window or a key split can leave a row with no key: O = 0 and
         // LSE = -inf (log of an empty sum)
         constexpr bool MAY_BE_EMPTY = WINDOW || SPLIT;
@@ -1004,7 +915,7 @@ hipError_t launch_direct(const void* q, const void* k, const void* v, void* o, f
     hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, false>), dim3((unsigned)(nqb * BH)),
                        dim3(G::NT), 0, stream, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<uint16_t*>(o), lse, BH, Lq, Lk, nqb, scale * kLog2e, wl, wr,
+                       static_cast<uint16_t*>(o), lse, BH, Lq, Lk, nqb, exp2_factor(scale * (double)kLog2e), wl, wr,
                        1, nullptr, nullptr);
     return hipGetLastError();
 }
@@ -1052,7 +963,7 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
                        dim3((unsigned)(nqb * BH * nsplit)), dim3(G::NT), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq,
-                       Lk, nqb, scale * kLog2e, 0, 0, nsplit, opart, lpart);
+                       Lk, nqb, exp2_factor(scale * (double)kLog2e), 0, 0, nsplit, opart, lpart);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int rows = BH * Lq;
@@ -1085,7 +996,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o,
     const int BH = B * H;
     const int nqb = (Lq + G::BM - 1) / G::BM;
     const long long nblocks = (long long)nqb * BH;
-    const float c = scale * kLog2e;
+    const float c = exp2_factor(scale * (double)kLog2e);
     hipLaunchKernelGGL((fa_fwd_kernel<E, D, CAUSAL>), dim3((unsigned)nblocks),
                        dim3(G::NT), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k),
@@ -1103,21 +1014,14 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
                   : launch_one<E, D, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, stream);
 }
 
-template <class E>
-hipError_t launch_e(const void* q, const void* k, const void* v, void* o,
-                    float* lse, int B, int H, int Lq, int Lk, int d,
-                    bool causal, float scale, hipStream_t stream)
+hipError_t launch_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int Lq, int Lk, int d, bool causal, float scale,
+                      hipStream_t stream)
 {
-#ifndef FA_NO_DIRECT
-    if constexpr (std::is_same<E, BF16>::value) {
-        return causal ? launch_direct_d<kCausal>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream)
-                      : launch_direct_d<kFull>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream);
-    }
-#endif
     switch (d) {
-    case 64:  return launch_d<E, 64>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
-    case 128: return launch_d<E, 128>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
-    case 256: return launch_d<E, 256>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    case 64:  return launch_d<F32, 64>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    case 128: return launch_d<F32, 128>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
+    case 256: return launch_d<F32, 256>(q, k, v, o, lse, B, H, Lq, Lk, causal, scale, stream);
     default:  return hipErrorInvalidValue;
     }
 }
@@ -1133,15 +1037,9 @@ bool tile_config(DType dt, int d, TileConfig* out)
 {
     if (dt == DType::BF16) {
         switch (d) {
-#ifndef FA_NO_DIRECT
         case 64:  *out = TileConfig{DGeom<64>::BM, DGeom<64>::BN, DGeom<64>::NT}; return true;
         case 128: *out = TileConfig{DGeom<128>::BM, DGeom<128>::BN, DGeom<128>::NT}; return true;
         case 256: *out = TileConfig{DGeom<256>::BM, DGeom<256>::BN, DGeom<256>::NT}; return true;
-#else
-        case 64:  *out = cfg_of<BF16, 64>();  return true;
-        case 128: *out = cfg_of<BF16, 128>(); return true;
-        case 256: *out = cfg_of<BF16, 256>(); return true;
-#endif
         }
     } else if (dt == DType::F32) {
         switch (d) {
@@ -1158,8 +1056,9 @@ hipError_t launch_fwd(DType dt, const void* q, const void* k, const void* v,
                       int d, bool causal, float scale, hipStream_t stream)
 {
     if (dt == DType::BF16)
-        return launch_e<BF16>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
-    return launch_e<F32>(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
+        return causal ? launch_direct_d<kCausal>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream)
+                      : launch_direct_d<kFull>(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 0, stream);
+    return launch_f32(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, stream);
 }
 
 hipError_t launch_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -3,9 +3,22 @@
 // Not installed, not part of the ABI.
 #pragma once
 
+#include <cfloat>
+
 #include <hip/hip_runtime_api.h>
 
 namespace fa {
+
+// Exponent factor of the scores, c = scale * log2(e) (the exp2 form of exp).
+// The kernels mask a score with -inf and form fma(S, c, -m), which is NaN
+// for c = 0, so a factor below FLT_MIN (in practice scale = 0) is raised to
+// FLT_MIN = 2^-126: every score with |S| < 2^101 then has an exponent within
+// 2^-25 of its row's reference, exp2 of it is exactly 1 in fp32, and every
+// visible key weighs the same, which is the result for scale = 0.
+inline float exp2_factor(double scale_log2e) {
+    const float c = (float)scale_log2e;
+    return c < FLT_MIN ? FLT_MIN : c;
+}
 
 enum class DType { BF16 = 0, F32 = 1 };
 

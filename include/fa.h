@@ -60,7 +60,8 @@ enum fa_status {
     FA_ERR_SHAPE = 2,          /* B, H, Lq or Lk < 1, or a size overflows    */
     FA_ERR_UNSUPPORTED_D = 3,  /* d is not 64, 128 or 256                    */
     FA_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned           */
-    FA_ERR_SCALE = 5,          /* scale is not finite and > 0                */
+    FA_ERR_SCALE = 5,          /* scale not finite and >= 0 (fa_bwd: > 0;
+                                  fa_fwd_fp8: descales finite and > 0)      */
     FA_ERR_ARG = 6,            /* causal not 0/1, a window bound < -1, or
                                   outputs overlap inputs                     */
     FA_ERR_LAUNCH = 7,         /* the kernel launch failed                   */
@@ -77,7 +78,10 @@ enum fa_status {
  * round to nearest even.
  *   d      : 64, 128 or 256
  *   causal : 0 (all keys) or 1 (key j visible to query i iff j <= i)
- *   scale  : multiplies QK^T; finite and > 0 (usually 1/sqrt(d))
+ *   scale  : multiplies QK^T; finite and >= 0 (usually 1/sqrt(d)).  scale = 0
+ *            weighs every visible key the same (O the mean of the visible V
+ *            rows, lse = ln of their count); the kernels then use the
+ *            exponent factor FLT_MIN in place of 0 (exact for |q.k| < 2^101).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int Lq, int Lk, int d, int causal, float scale,
@@ -158,7 +162,7 @@ int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_
  *     dv = P^T dout,   dP = dout v^T,   dS = P (dP - Delta),
  *     dq = scale dS k,  dk = scale dS^T q
  * o and lse must be the outputs of fa_fwd for the same q, k, v, causal and
- * scale (lse is the natural-log LSE fa_fwd writes).  Products run on bf16
+ * scale (lse is the natural-log LSE fa_fwd writes; scale > 0 here).  Products run on bf16
  * MFMA with fp32 accumulation (P and dS rounded to bf16 for their second
  * product); dq, dk, dv are written in bf16, round to nearest even.
  *   layout    : q, o, dout, dq [B, H, Lq, d]; k, v, dk, dv [B, H, Lk, d];
@@ -186,8 +190,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  *               decode(code) * q_descale (k_descale, v_descale for k, v)
  *   o         : bf16 [B, H, Lq, d];  lse: fp32 [B, H, Lq], natural log
  *   d         : 128 (other values: FA_ERR_UNSUPPORTED_D)
- *   descales  : finite and > 0, and scale * q_descale * k_descale finite and
- *               > 0 (else FA_ERR_SCALE)
+ *   descales  : finite and > 0; scale finite and >= 0, and scale * q_descale
+ *               * k_descale * log2(e) finite in fp32 (else FA_ERR_SCALE); a
+ *               product below FLT_MIN weighs every visible key the same
  * S = scale * q_descale * k_descale * (Q K^T) from the codes (their products
  * are exact, fp32 accumulation); the second product takes P multiplied by
  * 2^8 and rounded to E4M3 (nearest even), while the row sum uses the

@@ -38,8 +38,16 @@ Two functions pin such a kernel from two sides:
       with P_ij = p_j / l_i the exact softmax weights.
 
 Both take an optional bound on the error of S itself, s_err: |s~_ij - s_ij|
-<= s_err * scale * sum_t |q_it| |k_jt| (a matrix unit that accumulates the
-products with less than fp32 precision).  With D_i = max_j of that bound,
+<= s_err * scale * sum_t |q_it| |k_jt|.  Its value comes from a stated model
+of the matrix unit, not from measuring it: each product of two E4M3 values
+is exact in fp32 (at most 8 significant bits, exponents within range), and
+the d products of a score are added in some order, each addition rounded to
+fp32's 24-bit significand in some direction (the accumulator format the
+instruction names; round-to-nearest is not assumed).  Any such sum is
+within gamma_{d-1} sum_t |q_t k_t| of the exact one, gamma_k = k u / (1 - k
+u) with u = 2^-23 (fp32_sum_error_factor: the recursive-summation bound of
+N. J. Higham, "Accuracy and Stability of Numerical Algorithms", 2nd ed.,
+section 4.2, with the unit roundoff of directed rounding).  With D_i = max_j of that bound,
 every p_j moves by a factor within e^(+-D_i) (its score and the max both
 move), which adds (e^(2 D_i) - 1)(sum_j P_ij |v_jd| + |O_id|) to the bound
 and scales its rounding terms by e^(2 D_i); the blocked algorithm then also
@@ -56,6 +64,21 @@ import numpy as np
 
 E4M3_MAX = 448.0
 P_SHIFT = 8   # P is rounded as P * 2^8
+# unit roundoff of fp32 (24-bit significand) under any rounding direction
+FP32_DIRECTED_U = 2.0 ** -23
+# key-block size of the blocked algorithm when it serves as a diagnostic
+# beside the exact definition (a fixed choice, 128 keys; pass/fail never
+# depends on it)
+FP8_DIAG_BLOCK = 128
+
+
+def fp32_sum_error_factor(n: int) -> float:
+    """gamma_{n-1} = (n - 1) u / (1 - (n - 1) u), u = 2^-23: any fp32 sum of n
+    terms, in any order, every addition rounded in any direction, lies
+    within gamma_{n-1} sum_i |x_i| of the exact sum (Higham, "Accuracy and
+    Stability of Numerical Algorithms", 2nd ed., section 4.2)."""
+    k = n - 1
+    return k * FP32_DIRECTED_U / (1.0 - k * FP32_DIRECTED_U)
 
 
 def e4m3_round(x):
@@ -203,4 +226,4 @@ def fp8_flops(Lq: int, Lk: int, d: int, causal: bool) -> float:
 
 
 __all__ = ["e4m3_round", "attention_fp8_blocked", "fp8_error_bound", "fp8_flops",
-           "E4M3_MAX", "P_SHIFT"]
+           "fp32_sum_error_factor", "E4M3_MAX", "P_SHIFT", "FP32_DIRECTED_U", "FP8_DIAG_BLOCK"]

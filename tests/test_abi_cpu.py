@@ -63,6 +63,9 @@ def test_tile_config():
     with pytest.raises(fa.FAError):
         fa.tile_config("bf16", 96)
     bm, bn, th = fa.tile_config("fp8", 128)
+    # the FP8 kernel's key tile is the block the blocked FP8 diagnostic uses
+    from oracle.attention_fp8 import FP8_DIAG_BLOCK
+    assert bn == FP8_DIAG_BLOCK
     assert bm % 32 == 0 and bn % 64 == 0 and bm % (th // 64 * 32) == 0
     for d in (64, 256):
         with pytest.raises(fa.FAError):
@@ -90,8 +93,10 @@ def test_validation_errors(fn):
         assert _st(fn, d=d) == 3
     assert _st(fn, k=K + 8) == 4
     assert _st(fn, o=O + 2) == 4
-    for s in (0.0, -0.5, math.inf, math.nan):
+    for s in (-0.5, -0.0 - 1e-30, math.inf, math.nan):
         assert _st(fn, scale=s) == 5
+    # scale = 0 is accepted (the check after it fails instead)
+    assert _st(fn, scale=0.0, causal=2) == 6
     assert _st(fn, causal=2) == 6
     assert _st(fn, causal=-1) == 6
     # outputs overlapping an input or each other
@@ -215,11 +220,16 @@ def test_fp8_validation_errors():
         assert _st_fp8(d=d) == 3
     assert _st_fp8(q=Q + 8) == 4
     for name in ("scale", "q_descale", "k_descale", "v_descale"):
-        for x in (0.0, -1.0, math.inf, math.nan):
+        for x in (-1.0, math.inf, math.nan):
             assert _st_fp8(**{name: x}) == 5
-    # the combined exponent factor overflows / underflows fp32
+    for name in ("q_descale", "k_descale", "v_descale"):
+        assert _st_fp8(**{name: 0.0}) == 5
+    # scale = 0 is accepted (the check after it fails instead)
+    assert _st_fp8(scale=0.0, causal=3) == 6
+    # the combined exponent factor overflows fp32; one that underflows
+    # weighs every key the same, as scale = 0 does
     assert _st_fp8(q_descale=1e30, k_descale=1e30) == 5
-    assert _st_fp8(q_descale=1e-30, k_descale=1e-30) == 5
+    assert _st_fp8(q_descale=1e-30, k_descale=1e-30, causal=3) == 6
     assert _st_fp8(causal=3) == 6
     # o is bf16 (2 bytes per element) over 1-byte inputs: o = [Q, Q + 2 |q|)
     assert _st_fp8(k=Q + 2 * 2 * 128 * 128 - 16, o=Q, q=O) == 6

