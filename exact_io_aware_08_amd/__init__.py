@@ -25,7 +25,7 @@ STATUS_NAMES = {
 }
 # every function the C header declares
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_splitkv",
-           "fa_splitkv_workspace_size", "fa_splitkv_suggest", "fa_bwd", "fa_bwd_workspace_size",
+           "fa_fwd_splitkv_noalloc", "fa_noalloc_scratch_bytes", "fa_splitkv_workspace_size", "fa_splitkv_suggest", "fa_bwd", "fa_bwd_workspace_size",
            "fa_status_string", "fa_abi_version", "fa_tile_config")
 
 
@@ -75,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_fwd_splitkv.restype = i
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = i
+    lib.fa_noalloc_scratch_bytes.argtypes = []
+    lib.fa_noalloc_scratch_bytes.restype = sz
     lib.fa_splitkv_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_splitkv_workspace_size.restype = sz
     lib.fa_splitkv_suggest.argtypes = [i, i, i, i, i, i, i]
@@ -213,6 +217,24 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, num_splits,
     return st
 
 
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Lq, Lk, d, causal, scale, num_splits,
+                           stream=None):
+    """bf16 key-split forward through the C ABI (``fa_fwd_splitkv_noalloc``):
+    the partials go to the library's fixed per-GPU scratch, so nothing is
+    allocated; calls that overlap on one GPU race."""
+    st = load_library().fa_fwd_splitkv_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Lq),
+        int(Lk), int(d), int(causal), float(scale), int(num_splits), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, status_string(st))
+    return st
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed scratch ``fa_fwd_splitkv_noalloc`` uses per GPU."""
+    return int(load_library().fa_noalloc_scratch_bytes())
+
+
 def bwd_workspace_size(B, H, Lq) -> int:
     """Bytes of workspace fa_bwd needs (0: invalid arguments)."""
     return int(load_library().fa_bwd_workspace_size(int(B), int(H), int(Lq)))
@@ -282,6 +304,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
 
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_window", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_noalloc", "noalloc_scratch_bytes",
            "splitkv_workspace_size", "splitkv_suggest", "fa_bwd", "bwd_workspace_size",
            "attention",
            "status_string",

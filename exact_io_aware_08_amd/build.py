@@ -21,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_fwd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["fa_fwd_kernel.hip", "fa_fp8_kernel.hip", "fa_bwd_kernel.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd_kernel.hip", "fa_fp8_kernel.hip", "fa_bwd_kernel.hip", "fa_noalloc.hip",
+           "fa_api.cpp"]
 ARCH = "gfx950"
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

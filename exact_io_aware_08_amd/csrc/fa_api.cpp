@@ -46,6 +46,7 @@ struct MaskSpec {
     int nsplit = 0;        // fa_fwd_splitkv: key splits (>= 1), else 0
     void* workspace = nullptr;
     std::size_t workspace_bytes = 0;
+    bool check_only = false;   // run the argument checks (not the workspace's), launch nothing
 };
 
 int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
@@ -61,7 +62,7 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         return FA_ERR_ALIGN;
     if (!std::isfinite(scale) || !(scale >= 0.f)) return FA_ERR_SCALE;
     if (mask_status != FA_OK) return mask_status;   // causal / window / split arguments
-    if (mask.nsplit) {
+    if (mask.nsplit && !mask.check_only) {
         if (!mask.workspace) return FA_ERR_NULL;
         if (!aligned16(mask.workspace)) return FA_ERR_ALIGN;
     }
@@ -82,6 +83,7 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
         overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
         overlaps(lse, lbytes, o, qbytes))
         return FA_ERR_ARG;
+    if (mask.check_only) return FA_OK;
     if (mask.nsplit) {
         const std::size_t wbytes = split_workspace_bytes(bh, Lq, d, mask.nsplit);
         if (mask.workspace_bytes < wbytes) return FA_ERR_WORKSPACE;
@@ -136,6 +138,21 @@ std::size_t bwd_workspace_bytes(long long bh, int Lq) {
 }
 
 }  // namespace
+
+namespace fa {
+
+int splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int Lq, int Lk, int d, int causal, float scale, int num_splits) {
+    MaskSpec m;
+    int ms = causal_mask(causal, &m);
+    if (ms == FA_OK && (num_splits < 1 || num_splits > kMaxSplits)) ms = FA_ERR_ARG;
+    m.nsplit = num_splits;
+    m.check_only = true;
+    return validate_and_launch(DType::BF16, 2, q, k, v, o, lse, B, H, Lq, Lk, d, ms, m, scale,
+                               nullptr);
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -279,6 +296,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, 1 <= num_splits <= 64, and outputs and workspace must not overlap inputs";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size";
+    case FA_ERR_SCRATCH:
+        return "the key-split partials exceed the library's fixed scratch "
+               "(fa_noalloc_scratch_bytes)";
     default: return "unknown status";
     }
 }

@@ -51,6 +51,11 @@ hipError_t launch_fwd_split(const void* q, const void* k, const void* v, void* o
                             int B, int H, int Lq, int Lk, int d, bool causal, float scale,
                             int nsplit, float* opart, float* lpart, hipStream_t stream);
 
+// Every argument check of fa_fwd_splitkv except those of the workspace;
+// enqueues nothing.  FA_OK or the status fa_fwd_splitkv would return.
+int splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int H, int Lq, int Lk, int d, int causal, float scale, int num_splits);
+
 // FP8 (E4M3) forward: tile geometry for head dim d (false: no instantiation).
 bool fp8_tile_config(int d, TileConfig* out);
 

@@ -51,8 +51,9 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd;
-                              5: fa_fwd_fp8; 6: fa_splitkv_suggest */
+#define FA_ABI_VERSION 7   /* 2: fa_fwd_window; 3: fa_fwd_splitkv; 4: fa_bwd;
+                              5: fa_fwd_fp8; 6: fa_splitkv_suggest;
+                              7: fa_fwd_splitkv_noalloc */
 
 enum fa_status {
     FA_OK = 0,
@@ -65,7 +66,9 @@ enum fa_status {
     FA_ERR_ARG = 6,            /* causal not 0/1, a window bound < -1, or
                                   outputs overlap inputs                     */
     FA_ERR_LAUNCH = 7,         /* the kernel launch failed                   */
-    FA_ERR_WORKSPACE = 8       /* workspace smaller than required            */
+    FA_ERR_WORKSPACE = 8,      /* workspace smaller than required            */
+    FA_ERR_SCRATCH = 9         /* fa_fwd_splitkv_noalloc: the partials exceed
+                                  the fixed scratch (fa_noalloc_scratch_bytes) */
 };
 
 /*
@@ -139,6 +142,26 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int Lq, int Lk, int d, int causal, float scale,
                    int num_splits, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The fp32 partials live in a
+ * fixed device array of the library, fa_noalloc_scratch_bytes() bytes (40
+ * MiB) on each GPU it runs on, held until the process ends; the call
+ * itself allocates and frees nothing.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap in time on one GPU race; calls on
+ * different GPUs do not.  All arguments, checks, results and errors as
+ * fa_fwd_splitkv (same kernels, bit-identical output); a problem whose
+ * partials, fa_splitkv_workspace_size(B, H, Lq, d, num_splits) bytes,
+ * exceed the array returns FA_ERR_SCRATCH before any HIP call.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Lq, int Lk, int d, int causal, float scale,
+                           int num_splits, hipStream_t stream);
+
+/* Bytes of the fixed scratch fa_fwd_splitkv_noalloc uses per GPU.  Host-only. */
+size_t fa_noalloc_scratch_bytes(void);
 
 /* Workspace bytes fa_fwd_splitkv needs, or 0 for invalid arguments
  * (B, H, Lq < 1, d not 64/128/256, num_splits outside 1 .. 64).  Host-only. */

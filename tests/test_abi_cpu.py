@@ -49,7 +49,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for st in range(9):
+    for st in range(10):
         assert fa.status_string(st) != "unknown status"
     assert fa.status_string(99) == "unknown status"
 
@@ -165,6 +165,37 @@ def test_splitkv_validation_errors():
     assert _st_split(workspace_bytes=need - 1) == 8
     assert _st_split(workspace=Q + 256) == 6         # overlaps q
     assert _st_split(d=32) == 3
+
+
+def _st_noalloc(**kw):
+    args = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Lq=128, Lk=128, d=64,
+                causal=0, scale=0.125, num_splits=4)
+    args.update(kw)
+    try:
+        fa.fa_fwd_splitkv_noalloc(**args)
+    except fa.FAError as e:
+        return e.status
+    raise AssertionError("call was expected to fail validation")
+
+
+def test_noalloc_validation_errors():
+    # the ordinary key-split checks run first, on the host
+    assert fa.noalloc_scratch_bytes() == 40 << 20
+    assert _st_noalloc(q=0) == 1
+    assert _st_noalloc(B=0) == 2
+    assert _st_noalloc(d=96) == 3
+    assert _st_noalloc(o=O + 2) == 4
+    assert _st_noalloc(scale=-1.0) == 5
+    assert _st_noalloc(causal=2) == 6
+    for n in (0, 65):
+        assert _st_noalloc(num_splits=n) == 6
+    assert _st_noalloc(o=Q + 256) == 6
+    # partials beyond the fixed scratch: a clear error, before any HIP call
+    cap = fa.noalloc_scratch_bytes()
+    big = dict(B=1, H=16, Lq=4096, Lk=65536, d=128, num_splits=8)
+    assert fa.splitkv_workspace_size(1, 16, 4096, 128, 8) > cap
+    assert _st_noalloc(**big) == 9
+    assert "scratch" in fa.status_string(9)
 
 
 DO, DQ, DK, DV, WB = (0x10000000 * i for i in range(8, 13))
