@@ -257,11 +257,17 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
               stream=None, window=None, num_splits: int | None = None):
     """Convenience wrapper on torch tensors [B,H,L,d] (bf16 or fp32, on the
     GPU, contiguous): allocates O and LSE with torch and calls the C ABI on
-    ``stream`` (default: torch's current stream).  ``window``: optional
-    (left, right) sliding window, None on a side for no bound (bf16 only;
-    combined with ``causal`` the right bound is 0).  ``num_splits``: split
-    the keys among that many workgroups per query block and merge (bf16
-    only; the workspace is allocated with torch).  Returns (O, LSE)."""
+    ``stream`` (a torch stream or a raw handle; default: torch's current
+    stream).  On another stream than the current one, the launch stream
+    first waits for the current stream's work, O, LSE and the workspace are
+    allocated on the launch stream (so torch never hands their memory to
+    other work while the kernels run), and q, k, v are recorded as used
+    there; the caller synchronises before reading O and LSE on another
+    stream, as with any torch side stream.  ``window``: optional (left,
+    right) sliding window, None on a side for no bound (bf16 only; combined
+    with ``causal`` the right bound is 0).  ``num_splits``: split the keys
+    among that many workgroups per query block and merge (bf16 only; the
+    workspace is allocated with torch).  Returns (O, LSE)."""
     import torch
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, L, d]")
@@ -273,8 +279,24 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
         raise ValueError("k and v must be [B, H, Lk, d] matching q")
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    current = torch.cuda.current_stream(q.device)
     if stream is None:
-        stream = torch.cuda.current_stream(q.device)
+        stream = current
+    elif isinstance(stream, int):
+        stream = torch.cuda.ExternalStream(stream, device=q.device)
+    if stream != current:
+        stream.wait_stream(current)
+        for t in (q, k, v):
+            t.record_stream(stream)
+    with torch.cuda.stream(stream):
+        return _attention_on(q, k, v, causal, scale, stream, window, num_splits, B, H, Lq,
+                             Lk, d)
+
+
+def _attention_on(q, k, v, causal, scale, stream, window, num_splits, B, H, Lq, Lk, d):
+    # body of attention(): runs with `stream` as torch's current stream, so
+    # every allocation below belongs to it
+    import torch
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     if num_splits is not None:

@@ -233,6 +233,32 @@ def test_deterministic_and_stream():
     np.testing.assert_array_equal(L1, L2)
 
 
+def test_attention_side_stream_split_then_current_stream_allocations():
+    """attention() on a side stream with key splits: its outputs and
+    workspace belong to that stream, so allocations and writes on the
+    current stream right after the call cannot land in memory the split
+    kernels still use; the result equals the default-stream call bit for
+    bit and matches the oracle."""
+    import torch
+    q, k, v = make_inputs(37, 1, 4, 256, 4096, 128, "bf16")
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    o_ref, l_ref = fa.attention(qd, kd, vd, causal=False, num_splits=4)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for handle in (side, side.cuda_stream):
+        o2, l2 = fa.attention(qd, kd, vd, causal=False, num_splits=4, stream=handle)
+        # churn the current stream's pool while the side stream may still run
+        junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(8)]
+        del junk
+        side.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), False, f32_scale(128))
+    O = widen(o_ref.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.abs(O - O_ref).max() <= 2e-2
+    assert np.abs(l_ref.cpu().numpy() - L_ref).max() <= 1e-3
+
+
 def test_attention_wrapper_matches_abi():
     import torch
     q, k, v = make_inputs(35, 1, 2, 256, 256, 64, "bf16")
