@@ -15,16 +15,29 @@ is a reported baseline only.
 
 ``--workload fp8_causal_16k_d128`` runs the FP8 (E4M3) forward, fa_fwd_fp8,
 priced against the dense FP8 MFMA peak (5.0 PFLOP/s); its CPU baseline is
-the FP8 oracle (the blocked algorithm with E4M3-rounded P).
+the fp64 oracle on the dequantised inputs.
+
+The roofline object also carries the peak derived from this device (compute
+units x 4096 bf16 flops per clock x the maximum shader clock), the MFMA
+utilisation and HBM bytes of the committed rocprofv3 summaries (while their
+kernel-source hash matches), and, with ``--counters``, the same two figures
+from rocprofv3 passes over this bench in child processes.  The exit status
+is 1 when the result on the CPU sample is outside the parity bars.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
+import glob
 import hashlib
 import json
 import os
 import re
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -88,6 +101,84 @@ def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = Fal
     return float(t.group(1))
 
 
+def mfma_busy_from_profiles(workload: str, backward: bool = False, fp8: bool = False):
+    """MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x kernel
+    cycles) from the committed rocprofv3 SQ summary of this workload and
+    pass, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"fa_{'bwd' if backward else 'fwd'}_{workload}_sq_counters.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    b = re.search(r"MFMA busy per SIMD:[^=]*=\s*([0-9.]+)", text)
+    src = FP8_KERNEL_SOURCE if fp8 else BWD_KERNEL_SOURCE if backward else None
+    key = "fp8_kernel_source_sha256_16" if fp8 else \
+        "bwd_kernel_source_sha256_16" if backward else "kernel_source_sha256_16"
+    h = re.search(r"(?<![a-z0-9_])" + key + r":\s*([0-9a-f]+)", text)
+    if not b or not h or h.group(1) != kernel_source_hash(src):
+        return None
+    return float(b.group(1))
+
+
+def device_peak(cus: int):
+    """The bf16 dense MFMA peak derived from this device: compute units x
+    4096 flops per clock x the maximum shader clock (hipDeviceGetAttribute,
+    hipDeviceAttributeClockRate, in kHz)."""
+    khz = None
+    for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+        try:
+            hip = ctypes.CDLL(name)
+        except OSError:
+            continue
+        v = ctypes.c_int(0)
+        HIP_ATTR_CLOCK_RATE = 5   # hipDeviceAttributeClockRate
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), HIP_ATTR_CLOCK_RATE, 0) == 0 and v.value > 0:
+            khz = v.value
+        break
+    out = {"cus": cus, "bf16_flops_per_clk_per_cu": 4096,
+           "max_sclk_mhz": None if khz is None else khz / 1e3}
+    out["derived_bf16_tflops"] = None if khz is None else round(cus * 4096 * khz * 1e3 / 1e12, 1)
+    return out
+
+
+# counters of the in-run pass (one rocprofv3 run each; FETCH_SIZE reads half
+# the bytes a copy of known size moves, WRITE_SIZE all of them, so the byte
+# counters are scaled by 2 and 1)
+COUNTER_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"), ("FETCH_SIZE",),
+                  ("WRITE_SIZE",))
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def counters_in_run(argv, kernel_substr: str):
+    """rocprofv3 counter passes over this bench (child processes, the same
+    workload and mode, 3 steps): MFMA busy per SIMD and HBM bytes per launch
+    of the timed kernel.  None when rocprofv3 is not available."""
+    rp = shutil.which("rocprofv3")
+    if rp is None:
+        return None
+    vals = {}
+    child = [sys.executable, os.path.abspath(__file__), *argv, "--steps", "3", "--warmup", "1",
+             "--no-cpu-baseline", "--no-counters"]
+    for counters in COUNTER_PASSES:
+        with tempfile.TemporaryDirectory() as d:
+            cmd = [rp, "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "c",
+                   "--", *child]
+            subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                           timeout=300, cwd=tempfile.gettempdir())
+            for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                for r in csv.DictReader(open(f)):
+                    if kernel_substr in r["Kernel_Name"]:
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "FETCH_SIZE", "WRITE_SIZE")
+    if not all(vals.get(n) for n in need):
+        return None
+    mean = {n: float(np.mean(vals[n])) for n in need}
+    cycles = mean["GRBM_GUI_ACTIVE"] / 8          # summed over the 8 XCDs
+    return {"mfma_busy": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles), 4),
+            "hbm_bytes_per_launch": (FETCH_SCALE * mean["FETCH_SIZE"] +
+                                     WRITE_SCALE * mean["WRITE_SIZE"]) * 1024,
+            "passes": [" ".join(c) for c in COUNTER_PASSES]}
+
+
 def to_device(x: np.ndarray):
     """Host storage array (bf16 bits as uint16, or fp32) -> GPU tensor."""
     import torch
@@ -141,7 +232,7 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
     if max_heads:
         slices = slices[:max_heads]
     per_slice = algorithmic_flops(np.arange(w.Lq), w.Lk, w.d, causal, window)
-    spent, done, eo, el = 0.0, 0, 0.0, 0.0
+    spent, done, eo, el, omax, lmax = 0.0, 0, 0.0, 0.0, 0.0, 0.0
     for b, h in slices:
         qs, ks, vs = (widen(x[b:b + 1, h:h + 1]) for x in (q, k, v))
         t0 = time.perf_counter()
@@ -153,6 +244,8 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
         fin = np.isfinite(L_ref)
         el = max(el, float(np.abs(L_gpu[b:b + 1, h:h + 1].astype(np.float64)[fin]
                                   - L_ref[fin]).max()))
+        omax = max(omax, float(np.abs(O_ref).max()))
+        lmax = max(lmax, float(np.abs(L_ref[fin]).max()))
         if spent >= budget_s:
             break
     fl = done * per_slice
@@ -166,7 +259,8 @@ def cpu_baseline(w, causal, q, k, v, gpu_out, budget_s=15.0, max_heads=None,
                    f"{spent:.2f} s wall"),
         "seconds": spent,
         "sample_flops": fl,
-    }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "slices": done}
+    }, {"max_abs_err_O": eo, "max_abs_err_LSE": el, "max_abs_O_ref": omax,
+        "max_abs_LSE_ref": lmax, "slices": done}
 
 
 def cpu_baseline_fp8(w, causal, q8, k8, v8, ds, gpu_out, budget_s=15.0, max_heads=None):
@@ -281,6 +375,10 @@ def main(argv=None):
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="cap on (batch, head) slices in the CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="also run rocprofv3 counter passes (MFMA busy, HBM bytes) over "
+                         "this bench in child processes")
+    ap.add_argument("--no-counters", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device-to-device "
                          "copy of MIB MiB per step (the known-size reference "
@@ -302,9 +400,11 @@ def main(argv=None):
     props = torch.cuda.get_device_properties(0)
     sclk = getattr(props, "clock_rate", 0) / 1e3   # kHz -> MHz, where torch reports it
     cus = props.multi_processor_count
+    derived = device_peak(cus)
     log(f"bench: {props.name}: {cus} CUs" + (
-        f", max sclk {sclk:.0f} MHz -> {cus} x 4096 bf16 flops/clk x sclk = "
-        f"{cus * 4096 * sclk * 1e6 / 1e12:.1f} TFLOP/s dense bf16" if sclk else "") +
+        f", max sclk {derived['max_sclk_mhz']:.0f} MHz -> {cus} x 4096 bf16 flops/clk x sclk = "
+        f"{derived['derived_bf16_tflops']:.1f} TFLOP/s dense bf16"
+        if derived["derived_bf16_tflops"] else "") +
         "; the roofline uses the published peaks (bf16 2500, FP8 5000 TFLOP/s, HBM 8 TB/s)")
 
     w = WORKLOADS[a.workload]
@@ -458,6 +558,14 @@ def main(argv=None):
     })
     if hbm_bound:
         roofline["tflops_achieved"] = round(achieved, 3)
+    roofline["peak_derived_from_device"] = derived
+    roofline["mfma_busy"] = mfma_busy_from_profiles(w.name, backward, fp8)
+    if a.counters and not a.no_counters:
+        log("bench: rocprofv3 counter passes ...")
+        kname = "fa_bwd" if backward else "fa_fwd_fp8_kernel" if fp8 else \
+            "fa_fwd_direct_kernel" if w.dtype == "bf16" else "fa_fwd_kernel"
+        fwd_args = ["--workload", w.name, "--mode", mode]
+        roofline["counters_in_run"] = counters_in_run(fwd_args, kname)
 
     line = {
         "metric": METRIC,
@@ -483,12 +591,35 @@ def main(argv=None):
         "cpu_baseline": None if cpu is None else {
             k2: cpu[k2] for k2 in ("value", "unit", "cores", "kind", "sample")},
     }
+    ok = True
     if parity is not None:
         line["parity_on_cpu_sample"] = parity
+        ok = parity_ok(parity, w, backward, fp8)
+        line["parity_ok"] = ok
     if unsplit_ms is not None:
         line["unsplit_kernel_ms"] = round(unsplit_ms, 5)
     print(json.dumps(line), flush=True)
+    if not ok:
+        log("bench: the result on the CPU sample is outside the parity bars")
+        return 1
     return 0
+
+
+def parity_ok(parity: dict, w, backward: bool, fp8: bool) -> bool:
+    """The parity bars on the CPU sample: bf16 O 2e-2 and LSE 1e-3 absolute;
+    fp32 1e-5 of each tensor's largest magnitude; FP8 within the derived
+    bound and LSE 1e-3; backward 2e-2 of each gradient's largest
+    magnitude."""
+    if backward:
+        return all(parity[k] <= 2e-2 for k in ("max_rel_err_dQ", "max_rel_err_dK",
+                                               "max_rel_err_dV"))
+    if fp8:
+        return (parity["worst_ratio_to_fp8_bound_sampled_rows"] <= 1.0 and
+                parity["max_abs_err_LSE"] <= 1e-3)
+    if w.dtype == "fp32":
+        return (parity["max_abs_err_O"] <= 1e-5 * parity["max_abs_O_ref"] and
+                parity["max_abs_err_LSE"] <= 1e-5 * parity["max_abs_LSE_ref"])
+    return parity["max_abs_err_O"] <= 2e-2 and parity["max_abs_err_LSE"] <= 1e-3
 
 
 if __name__ == "__main__":
