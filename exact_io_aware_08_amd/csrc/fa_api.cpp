@@ -5,6 +5,7 @@
 // kernel launch and hipGetLastError right after it.
 
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
 #include <cmath>
 #include <cstddef>
@@ -140,6 +141,23 @@ std::size_t bwd_workspace_bytes(long long bh, int Lq) {
 }  // namespace
 
 namespace fa {
+
+int cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDev) {
+        const int n = cache[dev].load(std::memory_order_relaxed);
+        if (n > 0) return n;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 0;
+    if (dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
 
 int splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int H, int Lq, int Lk, int d, int causal, float scale, int num_splits) {
@@ -309,13 +327,7 @@ int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_
     if (B < 1 || H < 1 || Lq < 1 || Lk < 1 || (causal != 0 && causal != 1)) return 0;
     fa::TileConfig tc;
     if (!fa::tile_config(fa::DType::BF16, d, &tc)) return 0;
-    if (num_cus <= 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                hipSuccess || num_cus <= 0)
-            return 0;
-    }
+    if (num_cus <= 0 && (num_cus = fa::cu_count()) <= 0) return 0;
     const long long base = (long long)B * H * (((long long)Lq + tc.block_m - 1) / tc.block_m);
     if (base >= num_cus) return 1;
     // key tiles of the longest query block (causal: it sees min(Lk, Lq) keys)

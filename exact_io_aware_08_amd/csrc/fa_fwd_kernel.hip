@@ -420,9 +420,8 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // lanes (l%16)/4 + 4i (i = 0..3), so rows "4 keys x 4 d-quads" give every
 // lane 4 keys of its own d column; two such reads form one operand.
 // Tile rows at or beyond Lk arrive as zeros from the buffer's range check
-// (finite data that the mask turns into weight 0).  The two tile buffers
-// are separate LDS objects
-// and the key loop is unrolled by two, so each access names its buffer.
+// (finite data that the mask turns into weight 0).  The key loop is
+// unrolled by two, so each access names its buffer at a constant offset.
 // ===========================================================================
 
 // keys per tile, waves per workgroup, waves per SIMD the registers are
@@ -488,14 +487,21 @@ template <int D> struct DGeom {
 // in fp32 (Opart [nsplit][BH][Lq][D], Lpart [nsplit][BH][Lq], natural-log
 // LSE, O = 0 and LSE = -inf for a row that sees no key of the share), and
 // fa_merge_kernel combines the shares.
-template <int D, int MASK, bool SPLIT>
-__global__ __launch_bounds__((DGeom<D>::NT))
+//
+// KS = 2 (key halves): the workgroup holds two sets of NW waves on the same
+// query rows; set h takes the key tiles jlo + h, jlo + h + 2, ... through its
+// own pair of LDS buffers, and at the end set 1 hands its (m, l, O) to set 0
+// through LDS, which merges the two like two blocks of the online softmax
+// and writes the result.  That doubles the waves of a small grid and halves
+// the serial chain of tiles of each query block.
+template <int D, int MASK, bool SPLIT, int KS>
+__global__ __launch_bounds__((DGeom<D>::NT * KS))
 __attribute__((amdgpu_waves_per_eu(DGeom<D>::WPE, DGeom<D>::WPE)))
 void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                           const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
                           float* __restrict__ LSE, int BH, int Lq, int Lk, int nqb, float c,
                           int wl, int wr, int nsplit, float* __restrict__ Opart,
-                          float* __restrict__ Lpart)
+                          float* __restrict__ Lpart, int serp)
 {
     constexpr bool CAUSAL = MASK == kCausal;
     constexpr bool WINDOW = MASK == kWindow;
@@ -505,14 +511,21 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr int BN = G::BN, BM = G::BM, NS = G::NS, NMB = G::NMB, NDB = G::NDB;
     constexpr int CPR = G::CPR, NW = G::NW, NBQ = G::NBQ;
 
-    __shared__ __attribute__((aligned(1024))) uint16_t Kb0[G::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Kb1[G::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vb0[G::TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vb1[G::TILE];
+    static_assert(KS == 1 || (KS == 2 && !SPLIT), "key halves");
+    // K/V tile buffers, two per tensor, in one LDS object (every buffer
+    // address is then the object's base plus a constant, which spares
+    // address registers: 9 % faster at d = 256); with key halves, half h's
+    // tiles sit at h * TILE in each buffer
+    __shared__ __attribute__((aligned(1024))) uint16_t tiles[4 * KS * G::TILE];
+    uint16_t* const Kb0 = tiles;
+    uint16_t* const Kb1 = tiles + KS * G::TILE;
+    uint16_t* const Vb0 = tiles + 2 * KS * G::TILE;
+    uint16_t* const Vb1 = tiles + 3 * KS * G::TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = KS == 1 ? tid >> 6 : (tid >> 6) % NW;   // query rows of this wave
+    const int kh = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / NW;   // key half
     const int col = lane & 31;
     const int half = lane >> 5;
 
@@ -529,7 +542,20 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             bh /= nsplit;
         }
     }
-    const int qb = CAUSAL ? (nqb - 1 - lvl) : lvl;
+    // Causal: rank of the block's work among its head's blocks (0 = the
+    // longest rows).  Plainly the dispatch order.  When the whole grid is
+    // resident at once (serp > 0 levels per round), the blocks of a head
+    // are dealt to the CUs of its XCD in rounds of serp levels, one block
+    // per CU per round; alternate rounds run in reverse order (a serpentine
+    // deal), so the CU that takes the heaviest block of one round takes the
+    // lightest of the next and the work per CU evens out.
+    int rank = lvl;
+    if (CAUSAL && serp > 0) {
+        const int r = lvl / serp, i = lvl - r * serp;
+        const int m = min(serp, nqb - r * serp);   // levels in this round
+        rank = r * serp + ((r & 1) ? m - 1 - i : i);
+    }
+    const int qb = CAUSAL ? (nqb - 1 - rank) : lvl;
     const int q0 = qb * BM;
     const int q0w = q0 + wave * 32 * NBQ;   // query block nb: rows q0w + 32 nb + col
     const int qlast_w = q0w + 32 * NBQ - 1;
@@ -614,13 +640,15 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // below stay exact; the LDS destination comes from a scalar copy of the
     // wave index.
     const int swave = __builtin_amdgcn_readfirstlane(wave);
+    const int hofs = kh * G::TILE;   // this key half's buffers
     auto issue = [&](const uint16_t* Xh, int j, uint16_t* Xd, const unsigned (&ofs)[G::BPW]) {
         const int jc = min(j, nt - 1);   // j >= jlo
         const int bytes = j < nt ? min(BN, Lk - jc * BN) * D * 2 : 0;
         const uint16_t* base = Xh + (size_t)jc * BN * D;
 #pragma unroll
         for (int i = 0; i < G::BPW; ++i)
-            buffer_copy<16>(base, bytes, ofs[i], (FA_LDS void*)(Xd + (swave + NW * i) * 512));
+            buffer_copy<16>(base, bytes, ofs[i],
+                            (FA_LDS void*)(Xd + hofs + (swave + NW * i) * 512));
     };
     auto issue_k = [&](int j, uint16_t* Kd) { issue(Kh, j, Kd, kofs_g); };
     auto issue_v = [&](int j, uint16_t* Vd) { issue(Vh, j, Vd, vofs_g); };
@@ -633,7 +661,8 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr int NKF = NS < 8 ? NS : 8;
     int kfo[NKF];
 #pragma unroll
-    for (int st = 0; st < NKF; ++st) kfo[st] = col * D + (((2 * st + half) ^ G::f_k(col)) * 8);
+    for (int st = 0; st < NKF; ++st)
+        kfo[st] = hofs + col * D + (((2 * st + half) ^ G::f_k(col)) * 8);
     auto k_frag = [&](const uint16_t* Ks, int mb, int st) {
         return E::load(Ks + mb * 32 * D + kfo[st % NKF] + (st / NKF) * 128);
     };
@@ -650,7 +679,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int x = 0; x < G::NVL; ++x) {
         const int lc = 4 * x + 2 * vdh + (vq >> 1);
-        vlane[x] = (16 * vh + vi) * D + (lc ^ G::f_v(vi)) * 8 + (vq & 1) * 4;
+        vlane[x] = hofs + (16 * vh + vi) * D + (lc ^ G::f_v(vi)) * 8 + (vq & 1) * 4;
     }
     auto v_frag = [&](const uint16_t* Vs, int mb, int t, int db) {
         s16x4 u[2];
@@ -821,13 +850,15 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     using InFlight0 = std::integral_constant<int, 0>;
 
-    // every wave: S_j, softmax_j, PV_j; the copies of tile j+1 overlap them
+    // every wave: S_j, softmax_j, PV_j; the copies of its key half's next
+    // tile j + KS overlap them
     auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
         const int kv0 = j * BN;
-        issue_k(j + 1, Kn);
-        issue_v(j + 1, Vn);
-        // waves whose rows see no key of this tile skip its math
-        if ((!CAUSAL || kv0 <= qlast_w) &&
+        issue_k(j + KS, Kn);
+        issue_v(j + KS, Vn);
+        // waves whose rows see no key of this tile skip its math (with key
+        // halves, the last tile of half 1 may lie past the block's last one)
+        if ((KS == 1 || j < nt) && (!CAUSAL || kv0 <= qlast_w) &&
             (!WINDOW || (kv0 <= qlast_w + wr && kv0 + BN - 1 >= q0w - wl))) {
             f32x16 sacc[NBQ][NMB];
             s_tile(Kc, sacc);
@@ -853,16 +884,74 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         }
         sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
     };
-    issue_k(jlo, Kb0);
-    issue_v(jlo, Vb0);
+    // both key halves run the same steps (and barriers): half h takes tile
+    // jj + h of each pair jj
+    issue_k(jlo + kh, Kb0);
+    issue_v(jlo + kh, Vb0);
     sync_after(InFlight0{});
-    for (int j = jlo; j < nt; j += 2) {
-        step(j, Kb0, Vb0, Kb1, Vb1);
-        if (j + 1 < nt) step(j + 1, Kb1, Vb1, Kb0, Vb0);
+    for (int jj = jlo; jj < nt; jj += 2 * KS) {
+        step(jj + kh, Kb0, Vb0, Kb1, Vb1);
+        if (jj + KS < nt) step(jj + KS + kh, Kb1, Vb1, Kb0, Vb0);
     }
 
     // ---- epilogue: O / l, LSE = ln2 * (m + log2 l) -------------------------
     __builtin_amdgcn_s_waitcnt(0x0F70);   // no copy left in flight
+    if constexpr (KS == 2) {
+        // Merge of the key halves (the block-merge step of the online
+        // softmax): half 1 leaves (m, l, c, O) in LDS, lane by lane, and half
+        // 0 rescales both to m = max(m0, m1).  Every wave's copies landed
+        // (vmcnt(0) above) before the barrier, so the tile buffers are free:
+        // quad q of lane l of query wave w at ((w * NF/4 + q) * 64 + l) * 16
+        // bytes.
+        constexpr int NF = NBQ * (NDB * 16 + 4);   // floats per lane
+        static_assert(NF * 64 * NW * 4 <= 4 * KS * G::TILE * 2, "merge fits the tile buffers");
+        FA_LDS float* xs = (FA_LDS float*)(FA_LDS void*)tiles;
+        auto xq = [&](int q) {
+            return (FA_LDS f32x4*)(xs + ((wave * (NF / 4) + q) * 64 + lane) * 4);
+        };
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kh == 1) {
+#pragma unroll
+            for (int nb = 0; nb < NBQ; ++nb) {
+                const int q0q = nb * (NDB * 4 + 1);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *xq(q0q + db * 4 + g) = f32x4{oacc[nb][db][4 * g], oacc[nb][db][4 * g + 1],
+                                                     oacc[nb][db][4 * g + 2], oacc[nb][db][4 * g + 3]};
+                *xq(q0q + NDB * 4) = f32x4{m_run[nb], l_run[nb], c_run[nb], 0.f};
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): LDS writes done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kh == 1) return;
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            const int q0q = nb * (NDB * 4 + 1);
+            const f32x4 mlc = *xq(q0q + NDB * 4);
+            const float m = fmaxf(m_run[nb], mlc[0]);
+            const float mu = (m == -__builtin_inff()) ? 0.f : m;
+            const float a0 = __builtin_amdgcn_exp2f(m_run[nb] - mu);
+            const float a1 = __builtin_amdgcn_exp2f(mlc[0] - mu);
+            l_run[nb] = l_run[nb] * a0 + mlc[1] * a1;
+            c_run[nb] = c_run[nb] * a0 + mlc[2] * a1;
+            m_run[nb] = m;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 o1 = *xq(q0q + db * 4 + g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        oacc[nb][db][4 * g + e] = oacc[nb][db][4 * g + e] * a0 + o1[e] * a1;
+                }
+        }
+    }
     uint16_t* Oh = O + (size_t)bh * Lq * D;
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
@@ -912,12 +1001,31 @@ hipError_t launch_direct(const void* q, const void* k, const void* v, void* o, f
     using G = DGeom<D>;
     const int BH = B * H;
     const int nqb = (Lq + G::BM - 1) / G::BM;
-    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, false>), dim3((unsigned)(nqb * BH)),
-                       dim3(G::NT), 0, stream, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<uint16_t*>(o), lse, BH, Lq, Lk, nqb, exp2_factor(scale * (double)kLog2e), wl, wr,
-                       1, nullptr, nullptr);
-    return hipGetLastError();
+    const float c = exp2_factor(scale * (double)kLog2e);
+    const int cus = cu_count();
+    int serp = 0;
+    auto go = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(nqb * BH)), dim3(threads), 0, stream,
+                           static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH,
+                           Lq, Lk, nqb, c, wl, wr, 1, nullptr, nullptr, serp);
+        return hipGetLastError();
+    };
+    // d = 64 on a grid of at most two workgroups per CU: key halves, twice
+    // the waves per workgroup (two such workgroups fill a CU at four waves
+    // per SIMD, in 2 x 64 KB of LDS)
+    // The whole grid is then resident at once; causal, the blocks are dealt
+    // in serpentine order when every XCD's CUs take whole levels of its
+    // heads (heads per XCD dividing CUs per XCD).
+    if constexpr (D == 64) {
+        static_assert(4 * 2 * G::TILE * 2 * 2 <= 160 * 1024, "two workgroups per CU");
+        if ((long long)nqb * BH <= 2LL * cus) {
+            if (MASK == kCausal && BH % 8 == 0 && cus % 8 == 0 && (cus / 8) % (BH / 8) == 0)
+                serp = (cus / 8) / (BH / 8);
+            return go(fa_fwd_direct_kernel<D, MASK, false, 2>, 2 * G::NT);
+        }
+    }
+    return go(fa_fwd_direct_kernel<D, MASK, false, 1>, G::NT);
 }
 
 // ---- merge of key-split partials ------------------------------------------
@@ -959,11 +1067,11 @@ hipError_t launch_split(const void* q, const void* k, const void* v, void* o, fl
     using G = DGeom<D>;
     const int BH = B * H;
     const int nqb = (Lq + G::BM - 1) / G::BM;
-    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, true>),
+    hipLaunchKernelGGL((fa_fwd_direct_kernel<D, MASK, true, 1>),
                        dim3((unsigned)(nqb * BH * nsplit)), dim3(G::NT), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, Lq,
-                       Lk, nqb, exp2_factor(scale * (double)kLog2e), 0, 0, nsplit, opart, lpart);
+                       Lk, nqb, exp2_factor(scale * (double)kLog2e), 0, 0, nsplit, opart, lpart, 0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int rows = BH * Lq;

@@ -22,6 +22,10 @@ inline float exp2_factor(double scale_log2e) {
 
 enum class DType { BF16 = 0, F32 = 1 };
 
+// Compute units of the current device (cached per device); 0 if the query
+// fails.
+int cu_count();
+
 // Tile geometry of one compiled instantiation.
 struct TileConfig {
     int block_m;   // query rows per workgroup

@@ -92,6 +92,21 @@ def test_bf16_causal_1k_workload_full():
     full_case(w.seed, w.B, w.H, w.Lq, w.Lk, w.d, "bf16", True)
 
 
+# ---- d = 64 launch shapes ---------------------------------------------------
+
+@pytest.mark.parametrize("B,H,L,causal", [
+    (4, 16, 850, True),    # key halves, serpentine deal with a short last round
+    (8, 16, 512, True),    # key halves, two levels per round
+    (1, 40, 2048, True),   # above two workgroups per CU: one key set
+    (1, 40, 2048, False)])
+def test_bf16_d64_launch_shapes(B, H, L, causal):
+    """d = 64 grids of at most two workgroups per CU run two key halves per
+    workgroup (merged in LDS) and, causal, deal the query blocks to the CUs
+    in serpentine order; larger grids run one key set.  Every element
+    against the oracle in each regime."""
+    full_case(71, B, H, L, L, 64, "bf16", causal)
+
+
 # ---- a running max that rises slowly along the keys -----------------------
 
 @pytest.mark.parametrize("causal", [False, True])
