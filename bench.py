@@ -74,12 +74,24 @@ def kernel_source_hash(path: str = None) -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = False):
+def profile_path(kind: str, workload: str, mode: str | None, backward: bool):
+    """The committed summary of `kind` (hbm_counters, sq_counters) for this
+    workload: the one named for the workload and mode if present, else the
+    one named for the workload; None if neither exists."""
+    pre = os.path.join(PROFILES, f"fa_{'bwd' if backward else 'fwd'}_{workload}")
+    for path in ([f"{pre}_{mode}_{kind}.txt"] if mode else []) + [f"{pre}_{kind}.txt"]:
+        if os.path.exists(path):
+            return path
+    return None
+
+
+def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = False,
+                          mode: str | None = None):
     """HBM bytes per call from the committed rocprofv3 counter summary for
     this workload and pass, or None if absent or taken on a different
     kernel source."""
-    path = os.path.join(PROFILES, f"fa_{'bwd' if backward else 'fwd'}_{workload}_hbm_counters.txt")
-    if not os.path.exists(path):
+    path = profile_path("hbm_counters", workload, mode, backward)
+    if path is None:
         return None
     text = open(path).read()
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -101,12 +113,13 @@ def traffic_from_profiles(workload: str, backward: bool = False, fp8: bool = Fal
     return float(t.group(1))
 
 
-def mfma_busy_from_profiles(workload: str, backward: bool = False, fp8: bool = False):
+def mfma_busy_from_profiles(workload: str, backward: bool = False, fp8: bool = False,
+                            mode: str | None = None):
     """MFMA busy per SIMD (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x kernel
     cycles) from the committed rocprofv3 SQ summary of this workload and
     pass, or None if absent or taken on a different kernel source."""
-    path = os.path.join(PROFILES, f"fa_{'bwd' if backward else 'fwd'}_{workload}_sq_counters.txt")
-    if not os.path.exists(path):
+    path = profile_path("sq_counters", workload, mode, backward)
+    if path is None:
         return None
     text = open(path).read()
     b = re.search(r"MFMA busy per SIMD:[^=]*=\s*([0-9.]+)", text)
@@ -535,7 +548,7 @@ def main(argv=None):
     # flops per compulsory byte) is below the ridge point peak / 8 TB/s
     cbytes = compulsory_bytes(w, backward, fp8)
     hbm_bound = flops / cbytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    traffic = traffic_from_profiles(w.name, backward, fp8)
+    traffic = traffic_from_profiles(w.name, backward, fp8, mode)
     if hbm_bound:
         gbs = cbytes / (ms_kernel * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
@@ -559,7 +572,7 @@ def main(argv=None):
     if hbm_bound:
         roofline["tflops_achieved"] = round(achieved, 3)
     roofline["peak_derived_from_device"] = derived
-    roofline["mfma_busy"] = mfma_busy_from_profiles(w.name, backward, fp8)
+    roofline["mfma_busy"] = mfma_busy_from_profiles(w.name, backward, fp8, mode)
     if a.counters and not a.no_counters:
         log("bench: rocprofv3 counter passes ...")
         kname = "fa_bwd" if backward else "fa_fwd_fp8_kernel" if fp8 else \

@@ -82,3 +82,26 @@ def test_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     _profile(tmp_path, "fa_fwd_w8_hbm_counters.txt", fwd, bwd, stale)
     assert bench.traffic_from_profiles("w8", fp8=True) is None
     assert bench.traffic_from_profiles("absent") is None
+
+
+def test_profile_lookup_prefers_the_mode(tmp_path, monkeypatch):
+    """A summary named for the workload and mode is used for that mode; the
+    one named for the workload alone serves the other modes.  The MFMA busy
+    figure follows the same lookup and the same source hash."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    fwd = bench.kernel_source_hash()
+    stale = "0" * 16
+    _profile(tmp_path, "fa_fwd_w_hbm_counters.txt", fwd, stale, stale, nbytes=1.0e8)
+    _profile(tmp_path, "fa_fwd_w_noncausal_hbm_counters.txt", fwd, stale, stale, nbytes=2.0e8)
+    assert bench.traffic_from_profiles("w", mode="noncausal") == 2.0e8
+    assert bench.traffic_from_profiles("w", mode="causal") == 1.0e8
+    assert bench.traffic_from_profiles("w") == 1.0e8
+    (tmp_path / "fa_fwd_w_causal_sq_counters.txt").write_text(
+        f"# kernel_source_sha256_16: {fwd}\n"
+        "MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles) = 0.611\n")
+    assert bench.mfma_busy_from_profiles("w", mode="causal") == 0.611
+    assert bench.mfma_busy_from_profiles("w", mode="noncausal") is None
+    (tmp_path / "fa_fwd_w_causal_sq_counters.txt").write_text(
+        f"# kernel_source_sha256_16: {stale}\n"
+        "MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles) = 0.611\n")
+    assert bench.mfma_busy_from_profiles("w", mode="causal") is None
