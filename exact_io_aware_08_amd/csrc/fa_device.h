@@ -18,6 +18,9 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define FA_LDS __attribute__((address_space(3)))
+// on a kernel's lambdas: inline them at every call (an outlined lambda
+// would take its array arguments through scratch memory)
+#define FA_INLINE __attribute__((always_inline))
 
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e), base change of exp
 constexpr float kLn2 = 0.69314718055994531f;   // ln(2), LSE back to base e

@@ -436,13 +436,39 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // file (O alone is 128 registers): 8 waves of 32 rows, one softmax beside
 // the other wave's MFMAs, 16 % faster than 64-key tiles at one wave per
 // SIMD on the B=1 H=8 Lq=8000 Lk=8192 workload.
-template <int BN_, int NW_, int WPE_, int NBQ_> struct DCfgT {
+//
+// ONE: the four tile buffers live in one LDS object (each buffer address is
+// then the object's base plus a constant, which spares address registers:
+// the d = 256 kernel needs that to stay within 256 VGPRs, 9 % faster) or in
+// four (the compiler can then tell a buffer that a tile copy is filling
+// from the one being read, and does not wait for the copy before reading
+// V; with one object it does).
+template <int BN_, int NW_, int WPE_, int NBQ_, bool ONE_> struct DCfgT {
     static constexpr int BN = BN_, NW = NW_, WPE = WPE_, NBQ = NBQ_;
+    static constexpr bool ONE = ONE_;
 };
 template <int D> struct DCfg;
-template <> struct DCfg<64>  : DCfgT<64, 4, 4, 1> {};
-template <> struct DCfg<128> : DCfgT<128, 8, 2, 1> {};
-template <> struct DCfg<256> : DCfgT<32, 8, 2, 1> {};
+template <> struct DCfg<64>  : DCfgT<64, 4, 4, 1, false> {};
+template <> struct DCfg<128> : DCfgT<128, 8, 2, 1, false> {};
+template <> struct DCfg<256> : DCfgT<32, 8, 2, 1, true> {};
+
+// The four K/V tile buffers (N elements each): buf(i) for a constant i.
+template <int N, bool ONE> struct TileBufs;
+template <int N> struct TileBufs<N, true> {
+    __device__ static uint16_t* buf(int i) {
+        __shared__ __attribute__((aligned(1024))) uint16_t t[4 * N];
+        return t + i * N;
+    }
+};
+template <int N> struct TileBufs<N, false> {
+    __device__ static uint16_t* buf(int i) {
+        __shared__ __attribute__((aligned(1024))) uint16_t t0[N];
+        __shared__ __attribute__((aligned(1024))) uint16_t t1[N];
+        __shared__ __attribute__((aligned(1024))) uint16_t t2[N];
+        __shared__ __attribute__((aligned(1024))) uint16_t t3[N];
+        return i == 0 ? t0 : i == 1 ? t1 : i == 2 ? t2 : t3;
+    }
+};
 // Instruction schedule (measured): K fragments read ahead of their S MFMAs;
 // VALU instructions (the first exponentials) before the first PV MFMA; VALU
 // instructions beside each later PV MFMA.
@@ -512,15 +538,13 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     constexpr int CPR = G::CPR, NW = G::NW, NBQ = G::NBQ;
 
     static_assert(KS == 1 || (KS == 2 && !SPLIT), "key halves");
-    // K/V tile buffers, two per tensor, in one LDS object (every buffer
-    // address is then the object's base plus a constant, which spares
-    // address registers: 9 % faster at d = 256); with key halves, half h's
-    // tiles sit at h * TILE in each buffer
-    __shared__ __attribute__((aligned(1024))) uint16_t tiles[4 * KS * G::TILE];
-    uint16_t* const Kb0 = tiles;
-    uint16_t* const Kb1 = tiles + KS * G::TILE;
-    uint16_t* const Vb0 = tiles + 2 * KS * G::TILE;
-    uint16_t* const Vb1 = tiles + 3 * KS * G::TILE;
+    // K/V tile buffers, two per tensor; with key halves, half h's tiles sit
+    // at h * TILE in each buffer
+    using TB = TileBufs<KS * G::TILE, DCfg<D>::ONE>;
+    uint16_t* const Kb0 = TB::buf(0);
+    uint16_t* const Kb1 = TB::buf(1);
+    uint16_t* const Vb0 = TB::buf(2);
+    uint16_t* const Vb1 = TB::buf(3);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -641,7 +665,8 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // wave index.
     const int swave = __builtin_amdgcn_readfirstlane(wave);
     const int hofs = kh * G::TILE;   // this key half's buffers
-    auto issue = [&](const uint16_t* Xh, int j, uint16_t* Xd, const unsigned (&ofs)[G::BPW]) {
+    auto issue = [&](const uint16_t* Xh, int j, uint16_t* Xd,
+                     const unsigned (&ofs)[G::BPW]) FA_INLINE {
         const int jc = min(j, nt - 1);   // j >= jlo
         const int bytes = j < nt ? min(BN, Lk - jc * BN) * D * 2 : 0;
         const uint16_t* base = Xh + (size_t)jc * BN * D;
@@ -650,8 +675,8 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
             buffer_copy<16>(base, bytes, ofs[i],
                             (FA_LDS void*)(Xd + hofs + (swave + NW * i) * 512));
     };
-    auto issue_k = [&](int j, uint16_t* Kd) { issue(Kh, j, Kd, kofs_g); };
-    auto issue_v = [&](int j, uint16_t* Vd) { issue(Vh, j, Vd, vofs_g); };
+    auto issue_k = [&](int j, uint16_t* Kd) FA_INLINE { issue(Kh, j, Kd, kofs_g); };
+    auto issue_v = [&](int j, uint16_t* Vd) FA_INLINE { issue(Vh, j, Vd, vofs_g); };
     // K fragment (A operand of S^T) for d-step s of key block mb: slot row
     // mb*32 + col, logical chunk 2s + half; f_k(mb*32 + col) = f_k(col), so
     // mb only adds a whole-row offset and one lane offset per s suffices.
@@ -663,7 +688,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 #pragma unroll
     for (int st = 0; st < NKF; ++st)
         kfo[st] = hofs + col * D + (((2 * st + half) ^ G::f_k(col)) * 8);
-    auto k_frag = [&](const uint16_t* Ks, int mb, int st) {
+    auto k_frag = [&](const uint16_t* Ks, int mb, int st) FA_INLINE {
         return E::load(Ks + mb * 32 * D + kfo[st % NKF] + (st / NKF) * 128);
     };
     // V^T fragment for PV MFMA (mb, t, db): two transposed 8-byte reads.
@@ -681,7 +706,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         const int lc = 4 * x + 2 * vdh + (vq >> 1);
         vlane[x] = hofs + (16 * vh + vi) * D + (lc ^ G::f_v(vi)) * 8 + (vq & 1) * 4;
     }
-    auto v_frag = [&](const uint16_t* Vs, int mb, int t, int db) {
+    auto v_frag = [&](const uint16_t* Vs, int mb, int t, int db) FA_INLINE {
         s16x4 u[2];
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
@@ -696,7 +721,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     // ---- per-tile pieces ---------------------------------------------------
     // S^T = K Q^T for the wave's NBQ query blocks; each K fragment feeds NBQ
     // MFMAs and is read DPRE fragments ahead
-    auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NBQ][NMB]) {
+    auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NBQ][NMB]) FA_INLINE {
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
@@ -720,7 +745,8 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     // mask, running max and O rescale for query block nb; returns the max
     // used by the exponentials and sets alpha
-    auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha, float& hmax) {
+    auto row_max = [&](int kv0, int nb, f32x16 (&sacc)[NMB], float& alpha,
+                       float& hmax) FA_INLINE {
         const int qb0 = q0w + 32 * nb;
         // some key of the tile lies past Lk, right of a row's last key, or
         // (window) left of a row's first key
@@ -784,7 +810,8 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         return m_use;
     };
     // P = exp2(S c - m) as MFMA operands; returns this lane's partial sum
-    auto exps = [&](const f32x16 (&sacc)[NMB], float m_use, Frag (&pf)[NMB][2]) {
+    auto exps = [&](const f32x16 (&sacc)[NMB], float m_use,
+                    Frag (&pf)[NMB][2]) FA_INLINE {
         float rsum[NMB];
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
@@ -806,7 +833,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         return rs;
     };
     // O^T += V^T P^T; each V^T fragment feeds NBQ MFMAs
-    auto pv = [&](const uint16_t* Vc, const Frag (&pf)[NBQ][NMB][2]) {
+    auto pv = [&](const uint16_t* Vc, const Frag (&pf)[NBQ][NMB][2]) FA_INLINE {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -821,7 +848,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     // exponentials of key block 0 first, then each V^T fragment's MFMAs
     // with its two transposed reads and a share of the remaining VALU work
-    auto sched_pv_valu = [&]() {
+    auto sched_pv_valu = [&]() FA_INLINE {
         constexpr int NV = NMB * 2 * NDB;   // V^T fragments per tile
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPv0 * NBQ, 0);
@@ -850,37 +877,46 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
     };
     using InFlight0 = std::integral_constant<int, 0>;
 
+    // waves whose rows see no key of tile j skip its math (with key halves,
+    // the last tile of half 1 may lie past the block's last one)
+    auto sees = [&](int j) FA_INLINE {
+        const int kv0 = j * BN;
+        return (KS == 1 || j < nt) && (!CAUSAL || kv0 <= qlast_w) &&
+               (!WINDOW || (kv0 <= qlast_w + wr && kv0 + BN - 1 >= q0w - wl));
+    };
+    // softmax of tile j from its scores, then O += P V_j
+    auto soft_pv = [&](int j, f32x16 (&sacc)[NBQ][NMB], const uint16_t* Vc) FA_INLINE {
+        const int kv0 = j * BN;
+        float alpha[NBQ], rs[NBQ];
+        Frag pf[NBQ][NMB][2];
+        float dmax[NBQ];
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            float hmax;
+            const float m_use = row_max(kv0, nb, sacc[nb], alpha[nb], hmax);
+            rs[nb] = exps(sacc[nb], m_use, pf[nb]);
+            // bf16 rounding of P at this lane's tile maximum
+            const float pmx = __builtin_amdgcn_exp2f(__builtin_fmaf(hmax, c, -m_use));
+            dmax[nb] = (float)(__bf16)pmx - pmx;
+        }
+        pv(Vc, pf);
+        sched_pv_valu();
+#pragma unroll
+        for (int nb = 0; nb < NBQ; ++nb) {
+            l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
+            c_run[nb] = c_run[nb] * alpha[nb] + dmax[nb];
+        }
+    };
     // every wave: S_j, softmax_j, PV_j; the copies of its key half's next
     // tile j + KS overlap them
-    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) {
-        const int kv0 = j * BN;
+    auto step = [&](int j, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn,
+                    uint16_t* Vn) FA_INLINE {
         issue_k(j + KS, Kn);
         issue_v(j + KS, Vn);
-        // waves whose rows see no key of this tile skip its math (with key
-        // halves, the last tile of half 1 may lie past the block's last one)
-        if ((KS == 1 || j < nt) && (!CAUSAL || kv0 <= qlast_w) &&
-            (!WINDOW || (kv0 <= qlast_w + wr && kv0 + BN - 1 >= q0w - wl))) {
+        if (sees(j)) {
             f32x16 sacc[NBQ][NMB];
             s_tile(Kc, sacc);
-            float alpha[NBQ], rs[NBQ];
-            Frag pf[NBQ][NMB][2];
-            float dmax[NBQ];
-#pragma unroll
-            for (int nb = 0; nb < NBQ; ++nb) {
-                float hmax;
-                const float m_use = row_max(kv0, nb, sacc[nb], alpha[nb], hmax);
-                rs[nb] = exps(sacc[nb], m_use, pf[nb]);
-                // bf16 rounding of P at this lane's tile maximum
-                const float pmx = __builtin_amdgcn_exp2f(__builtin_fmaf(hmax, c, -m_use));
-                dmax[nb] = (float)(__bf16)pmx - pmx;
-            }
-            pv(Vc, pf);
-            sched_pv_valu();
-#pragma unroll
-            for (int nb = 0; nb < NBQ; ++nb) {
-                l_run[nb] = l_run[nb] * alpha[nb] + rs[nb];
-                c_run[nb] = c_run[nb] * alpha[nb] + dmax[nb];
-            }
+            soft_pv(j, sacc, Vc);
         }
         sync_after(InFlight0{});   // this wave's copies of tile j+1 landed
     };
@@ -901,14 +937,13 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
         // softmax): half 1 leaves (m, l, c, O) in LDS, lane by lane, and half
         // 0 rescales both to m = max(m0, m1).  Every wave's copies landed
         // (vmcnt(0) above) before the barrier, so the tile buffers are free:
-        // quad q of lane l of query wave w at ((w * NF/4 + q) * 64 + l) * 16
-        // bytes.
+        // query wave w's exchange goes through buffer w, quad q of lane l at
+        // (q * 64 + l) * 16 bytes.
         constexpr int NF = NBQ * (NDB * 16 + 4);   // floats per lane
-        static_assert(NF * 64 * NW * 4 <= 4 * KS * G::TILE * 2, "merge fits the tile buffers");
-        FA_LDS float* xs = (FA_LDS float*)(FA_LDS void*)tiles;
-        auto xq = [&](int q) {
-            return (FA_LDS f32x4*)(xs + ((wave * (NF / 4) + q) * 64 + lane) * 4);
-        };
+        static_assert(NW <= 4 && NF * 64 * 4 <= KS * G::TILE * 2, "merge fits the tile buffers");
+        uint16_t* const xb = wave == 0 ? Kb0 : wave == 1 ? Kb1 : wave == 2 ? Vb0 : Vb1;
+        FA_LDS float* xs = (FA_LDS float*)(FA_LDS void*)xb;
+        auto xq = [&](int q) { return (FA_LDS f32x4*)(xs + (q * 64 + lane) * 4); };
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
