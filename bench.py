@@ -161,14 +161,17 @@ COUNTER_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"), ("FETCH_SIZE"
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
-def counters_in_run(argv, kernel_substr: str):
+def counters_in_run(argv, kernels):
     """rocprofv3 counter passes over this bench (child processes, the same
-    workload and mode, 3 steps): MFMA busy per SIMD and HBM bytes per launch
-    of the timed kernel.  None when rocprofv3 is not available."""
+    workload and mode, 3 steps): MFMA busy per SIMD and HBM bytes per call
+    of the timed pass.  ``kernels``: the kernels that make up one call, each
+    given by name substrings joined with "&" (all must occur in the name);
+    each counter is averaged over each kernel's dispatches and the averages
+    summed.  None when rocprofv3 is not available."""
     rp = shutil.which("rocprofv3")
     if rp is None:
         return None
-    vals = {}
+    vals = {}   # (kernel, counter) -> values
     child = [sys.executable, os.path.abspath(__file__), *argv, "--steps", "3", "--warmup", "1",
              "--no-cpu-baseline", "--no-counters"]
     for counters in COUNTER_PASSES:
@@ -179,16 +182,19 @@ def counters_in_run(argv, kernel_substr: str):
                            timeout=300, cwd=tempfile.gettempdir())
             for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
                 for r in csv.DictReader(open(f)):
-                    if kernel_substr in r["Kernel_Name"]:
-                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                    for kn in kernels:
+                        if all(part in r["Kernel_Name"] for part in kn.split("&")):
+                            vals.setdefault((kn, r["Counter_Name"]), []).append(
+                                float(r["Counter_Value"]))
     need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "FETCH_SIZE", "WRITE_SIZE")
-    if not all(vals.get(n) for n in need):
+    if not all(vals.get((kn, n)) for kn in kernels for n in need):
         return None
-    mean = {n: float(np.mean(vals[n])) for n in need}
-    cycles = mean["GRBM_GUI_ACTIVE"] / 8          # summed over the 8 XCDs
-    return {"mfma_busy": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles), 4),
-            "hbm_bytes_per_launch": (FETCH_SCALE * mean["FETCH_SIZE"] +
-                                     WRITE_SCALE * mean["WRITE_SIZE"]) * 1024,
+    tot = {n: sum(float(np.mean(vals[(kn, n)])) for kn in kernels) for n in need}
+    cycles = tot["GRBM_GUI_ACTIVE"] / 8          # summed over the 8 XCDs
+    return {"mfma_busy": round(tot["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles), 4),
+            "hbm_bytes_per_launch": (FETCH_SCALE * tot["FETCH_SIZE"] +
+                                     WRITE_SCALE * tot["WRITE_SIZE"]) * 1024,
+            "kernels": list(kernels),
             "passes": [" ".join(c) for c in COUNTER_PASSES]}
 
 
@@ -575,10 +581,23 @@ def main(argv=None):
     roofline["mfma_busy"] = mfma_busy_from_profiles(w.name, backward, fp8, mode)
     if a.counters and not a.no_counters:
         log("bench: rocprofv3 counter passes ...")
-        kname = "fa_bwd" if backward else "fa_fwd_fp8_kernel" if fp8 else \
-            "fa_fwd_direct_kernel" if w.dtype == "bf16" else "fa_fwd_kernel"
+        if backward:
+            knames = ["fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq"]
+        elif fp8:
+            knames = ["fa_fwd_fp8_kernel"]
+        elif w.dtype != "bf16":
+            knames = ["fa_fwd_kernel"]
+        elif mode == "splitkv":
+            # the split instantiation only (the unsplit comparison run
+            # launches the same kernel name with SPLIT = false)
+            knames = ["fa_fwd_direct_kernel&, true,", "fa_merge_kernel"]
+        else:
+            knames = ["fa_fwd_direct_kernel"]
         fwd_args = ["--workload", w.name, "--mode", mode]
-        roofline["counters_in_run"] = counters_in_run(fwd_args, kname)
+        cr = counters_in_run(fwd_args, knames)
+        if cr is not None:
+            cr["hbm_gbs"] = round(cr["hbm_bytes_per_launch"] / (ms_kernel * 1e-3) / 1e9, 2)
+        roofline["counters_in_run"] = cr
 
     line = {
         "metric": METRIC,

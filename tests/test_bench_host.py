@@ -2,6 +2,7 @@
 against the measurement table's figures, the roofline bound each workload
 gets, and the one-GPU guard."""
 import math
+import os
 
 import pytest
 
@@ -105,3 +106,48 @@ def test_profile_lookup_prefers_the_mode(tmp_path, monkeypatch):
         f"# kernel_source_sha256_16: {stale}\n"
         "MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (1024 x cycles) = 0.611\n")
     assert bench.mfma_busy_from_profiles("w", mode="causal") is None
+
+
+def test_counters_in_run_sums_the_kernels_of_a_call(monkeypatch):
+    """The in-run counter passes average each counter over each named
+    kernel's dispatches and sum the averages over the kernels of one call;
+    MFMA busy is busy cycles over 1024 SIMDs x kernel cycles (GRBM_GUI_ACTIVE
+    summed over the 8 XCDs), HBM bytes are FETCH_SIZE x 2 + WRITE_SIZE x 1
+    KiB.  rocprofv3 is replaced by a writer of its CSV."""
+    import csv as _csv
+    values = {  # per kernel: counter -> per-dispatch values
+        "fa_a_kernel<1>": {"SQ_VALU_MFMA_BUSY_CYCLES": [1024 * 800.0, 1024 * 600.0],
+                           "GRBM_GUI_ACTIVE": [8 * 1000.0, 8 * 1000.0],
+                           "FETCH_SIZE": [100.0, 300.0], "WRITE_SIZE": [50.0, 50.0]},
+        "fa_b_kernel<1>": {"SQ_VALU_MFMA_BUSY_CYCLES": [0.0],
+                           "GRBM_GUI_ACTIVE": [8 * 1000.0],
+                           "FETCH_SIZE": [10.0], "WRITE_SIZE": [5.0]},
+        "other_kernel": {"SQ_VALU_MFMA_BUSY_CYCLES": [1e12], "GRBM_GUI_ACTIVE": [1.0],
+                         "FETCH_SIZE": [1e9], "WRITE_SIZE": [1e9]},
+    }
+
+    def fake_run(cmd, **kw):
+        d = cmd[cmd.index("-d") + 1]
+        pmc = cmd[cmd.index("--pmc") + 1:cmd.index("--output-format")]
+        with open(os.path.join(d, "c_counter_collection.csv"), "w", newline="") as f:
+            wr = _csv.writer(f)
+            wr.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            for kn, cv in values.items():
+                for c in pmc:
+                    for x in cv[c]:
+                        wr.writerow([kn, c, x])
+
+    monkeypatch.setattr(bench.shutil, "which", lambda name: "/usr/bin/rocprofv3")
+    monkeypatch.setattr(bench.subprocess, "run", fake_run)
+    r = bench.counters_in_run(["--workload", "w"], ["fa_a_kernel", "fa_b_kernel"])
+    # busy: (700 + 0) x 1024 / (1024 x (1000 + 1000)) = 0.35
+    assert r["mfma_busy"] == 0.35
+    # bytes: ((200 + 10) x 2 + (50 + 5)) KiB
+    assert r["hbm_bytes_per_launch"] == (210 * 2 + 55) * 1024
+    assert r["kernels"] == ["fa_a_kernel", "fa_b_kernel"]
+    # "&" joins substrings that must all occur: fa_a_kernel<2> is not <1>
+    values["fa_a_kernel<2>"] = {k: [x * 9 for x in v] for k, v in values["fa_a_kernel<1>"].items()}
+    r2 = bench.counters_in_run(["--workload", "w"], ["fa_a_kernel&<1>", "fa_b_kernel"])
+    assert r2["mfma_busy"] == 0.35 and r2["hbm_bytes_per_launch"] == r["hbm_bytes_per_launch"]
+    monkeypatch.setattr(bench.shutil, "which", lambda name: None)
+    assert bench.counters_in_run(["--workload", "w"], ["fa_a_kernel"]) is None
