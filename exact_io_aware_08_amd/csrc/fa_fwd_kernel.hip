@@ -429,9 +429,9 @@ void fa_fwd_kernel(const typename E::T* __restrict__ Q,
 // feeds that many MFMAs).  d = 64 runs 64-key tiles and 4-wave workgroups
 // (128 query rows) at four waves per SIMD (126 VGPRs, 32 KB of LDS each):
 // 3.5-6 % faster than 128-key tiles at two waves per SIMD on L = 4096 and
-// 16384, the same on the short causal B=4 H=16 L=1024 workload (20.4 us),
-// where 4-wave workgroups balance the triangular grid better than 8-wave
-// ones (21 us against 26 us).
+// 16384.  A d = 64 grid of at most two workgroups per CU instead runs two
+// key halves per workgroup (8 waves on the same 128 rows, see
+// launch_direct).
 // d = 256 takes 32-key tiles so that two waves per SIMD fit the register
 // file (O alone is 128 registers): 8 waves of 32 rows, one softmax beside
 // the other wave's MFMAs, 16 % faster than 64-key tiles at one wave per
