@@ -720,7 +720,7 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
 
     // ---- per-tile pieces ---------------------------------------------------
     // S^T = K Q^T for the wave's NBQ query blocks; each K fragment feeds NBQ
-    // MFMAs and is read DPRE fragments ahead
+    // MFMAs and is read kPreK fragments ahead
     auto s_tile = [&](const uint16_t* Kc, f32x16 (&sacc)[NBQ][NMB]) FA_INLINE {
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb)
@@ -955,8 +955,9 @@ void fa_fwd_direct_kernel(const uint16_t* __restrict__ Q, const uint16_t* __rest
                 for (int db = 0; db < NDB; ++db)
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
-                        *xq(q0q + db * 4 + g) = f32x4{oacc[nb][db][4 * g], oacc[nb][db][4 * g + 1],
-                                                     oacc[nb][db][4 * g + 2], oacc[nb][db][4 * g + 3]};
+                        *xq(q0q + db * 4 + g) =
+                            f32x4{oacc[nb][db][4 * g], oacc[nb][db][4 * g + 1],
+                                  oacc[nb][db][4 * g + 2], oacc[nb][db][4 * g + 3]};
                 *xq(q0q + NDB * 4) = f32x4{m_run[nb], l_run[nb], c_run[nb], 0.f};
             }
         }
