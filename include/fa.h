@@ -241,7 +241,10 @@ int fa_abi_version(void);
 /*
  * Tile geometry the library uses for (dtype, d): query rows per workgroup
  * (block_m), keys per K/V tile (block_n) and threads per workgroup.  dtype
- * is 0 for bf16, 1 for fp32, 2 for FP8 E4M3 (fa_fwd_fp8).  Returns FA_OK,
+ * is 0 for bf16, 1 for fp32, 2 for FP8 E4M3 (fa_fwd_fp8).  (A bf16 d = 64
+ * grid of at most two workgroups per compute unit runs the same rows and
+ * tiles with twice the threads: two sets of waves that split the key
+ * tiles between them.)  Returns FA_OK,
  * or FA_ERR_UNSUPPORTED_D /
  * FA_ERR_ARG for an unknown combination.  Host-only; makes no HIP call.
  */
