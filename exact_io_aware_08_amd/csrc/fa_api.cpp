@@ -20,6 +20,12 @@ bool aligned16(const void* p) {
     return (reinterpret_cast<std::uintptr_t>(p) & 15u) == 0;
 }
 
+// The kernels take the scores' exponent factor scale * log2(e) as an fp32
+// value; a scale above FLT_MAX / log2(e) would make it infinite.
+bool factor_finite(float scale) {
+    return std::isfinite((float)((double)scale * 1.4426950408889634));
+}
+
 // [p, p + bytes) overlaps [r, r + rbytes)
 bool overlaps(const void* p, std::size_t bytes, const void* r, std::size_t rbytes) {
     const auto a = reinterpret_cast<std::uintptr_t>(p);
@@ -61,7 +67,7 @@ int validate_and_launch(fa::DType dt, std::size_t esize, const void* q,
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
         !aligned16(lse))
         return FA_ERR_ALIGN;
-    if (!std::isfinite(scale) || !(scale >= 0.f)) return FA_ERR_SCALE;
+    if (!std::isfinite(scale) || !(scale >= 0.f) || !factor_finite(scale)) return FA_ERR_SCALE;
     if (mask_status != FA_OK) return mask_status;   // causal / window / split arguments
     if (mask.nsplit && !mask.check_only) {
         if (!mask.workspace) return FA_ERR_NULL;
@@ -274,7 +280,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
                           static_cast<const void*>(dq), static_cast<const void*>(dk),
                           static_cast<const void*>(dv), static_cast<const void*>(workspace)})
         if (!aligned16(p)) return FA_ERR_ALIGN;
-    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+    if (!std::isfinite(scale) || !(scale > 0.f) || !factor_finite(scale)) return FA_ERR_SCALE;
     if (causal != 0 && causal != 1) return FA_ERR_ARG;
     const long long bh = (long long)B * H;
     if (bh > (1LL << 30) || (long long)Lq * d > 0x7fffffffLL || (long long)Lk * d > 0x7fffffffLL ||
@@ -310,7 +316,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "B, H, Lq and Lk must be >= 1 and sizes must fit";
     case FA_ERR_UNSUPPORTED_D: return "head dim d must be 64, 128 or 256";
     case FA_ERR_ALIGN: return "pointers must be 16-byte aligned";
-    case FA_ERR_SCALE: return "scale must be finite and >= 0 (> 0 for fa_bwd; FP8 descales > 0)";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0 (> 0 for fa_bwd; FP8 descales > 0), with scale * log2(e) finite in fp32";
     case FA_ERR_ARG: return "causal must be 0 or 1, window bounds >= -1, 1 <= num_splits <= 64, and outputs and workspace must not overlap inputs";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_size";

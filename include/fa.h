@@ -62,7 +62,8 @@ enum fa_status {
     FA_ERR_UNSUPPORTED_D = 3,  /* d is not 64, 128 or 256                    */
     FA_ERR_ALIGN = 4,          /* a pointer is not 16-byte aligned           */
     FA_ERR_SCALE = 5,          /* scale not finite and >= 0 (fa_bwd: > 0;
-                                  fa_fwd_fp8: descales finite and > 0)      */
+                                  fa_fwd_fp8: descales finite and > 0), or
+                                  its exponent factor past fp32's range     */
     FA_ERR_ARG = 6,            /* causal not 0/1, a window bound < -1, or
                                   outputs overlap inputs                     */
     FA_ERR_LAUNCH = 7,         /* the kernel launch failed                   */
@@ -81,7 +82,8 @@ enum fa_status {
  * round to nearest even.
  *   d      : 64, 128 or 256
  *   causal : 0 (all keys) or 1 (key j visible to query i iff j <= i)
- *   scale  : multiplies QK^T; finite and >= 0 (usually 1/sqrt(d)).  scale = 0
+ *   scale  : multiplies QK^T; finite and >= 0 (usually 1/sqrt(d)), with
+ *            scale * log2(e) finite in fp32 (else FA_ERR_SCALE).  scale = 0
  *            weighs every visible key the same (O the mean of the visible V
  *            rows, lse = ln of their count); the kernels then use the
  *            exponent factor FLT_MIN in place of 0 (exact for |q.k| < 2^101).

@@ -95,6 +95,9 @@ def test_validation_errors(fn):
     assert _st(fn, o=O + 2) == 4
     for s in (-0.5, -0.0 - 1e-30, math.inf, math.nan):
         assert _st(fn, scale=s) == 5
+    # scale * log2(e) past fp32's range (the exponent factor would be inf)
+    assert _st(fn, scale=3e38) == 5
+    assert _st(fn, scale=2e38, causal=2) == 6
     # scale = 0 is accepted (the check after it fails instead)
     assert _st(fn, scale=0.0, causal=2) == 6
     assert _st(fn, causal=2) == 6
@@ -226,6 +229,7 @@ def test_bwd_validation_errors():
     assert _st_bwd(d=256) == 3 and _st_bwd(d=96) == 3
     assert _st_bwd(dq=DQ + 8) == 4
     assert _st_bwd(scale=0.0) == 5
+    assert _st_bwd(scale=3e38) == 5
     assert _st_bwd(causal=2) == 6
     assert _st_bwd(workspace_bytes=fa.bwd_workspace_size(1, 2, 128) - 1) == 8
     assert _st_bwd(dk=Q + 64) == 6         # an output overlapping an input
