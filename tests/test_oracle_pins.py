@@ -59,6 +59,40 @@ def test_brute_force(causal, Lq, Lk, d):
             np.testing.assert_allclose(L[b, 0], Lb, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_brute_force_seeded_sweep(seed):
+    """The definition by brute force over seeded random tiny problems: any
+    Lq, Lk in 1..10 and d in 1..5, B and H up to 2, full, causal or a random
+    window (either side unbounded or not, rows with no key included), scale
+    from 0 to 3 and scores up to 300 in magnitude (peaky rows)."""
+    rng = np.random.default_rng(7000 + seed)
+    for _ in range(12):
+        B, H = (int(x) for x in rng.integers(1, 3, size=2))
+        Lq, Lk = (int(x) for x in rng.integers(1, 11, size=2))
+        d = int(rng.integers(1, 6))
+        mode = ("full", "causal", "window")[int(rng.integers(3))]
+        scale = float(rng.choice([0.0, 0.05, 0.3, 1.0, 3.0]))
+        sigma = float(rng.choice([0.5, 1.0, 4.0, 10.0]))
+        q, k, v = (sigma * rng.standard_normal((B, H, n, d)) for n in (Lq, Lk, Lk))
+        # keep every score within math.exp's range (|s| <= 300)
+        smax = scale * np.abs(np.einsum("bhid,bhjd->bhij", q, k)).max()
+        if smax > 300.0:
+            q, k = q * math.sqrt(300.0 / smax), k * math.sqrt(300.0 / smax)
+        window = None
+        if mode == "window":
+            window = tuple(None if rng.random() < 0.25 else int(rng.integers(0, 6))
+                           for _ in range(2))
+        causal = mode == "causal"
+        O, L = attention_ref(q, k, v, causal, scale, window=window)
+        for b in range(B):
+            for h in range(H):
+                Ob, Lb = brute_force(q[b, h], k[b, h], v[b, h], causal, scale, window)
+                np.testing.assert_allclose(O[b, h], Ob, rtol=1e-12, atol=1e-12)
+                np.testing.assert_array_equal(np.isinf(L[b, h]), np.isinf(Lb))
+                fin = np.isfinite(Lb)
+                np.testing.assert_allclose(L[b, h][fin], Lb[fin], rtol=1e-13, atol=1e-12)
+
+
 # --- library routines ----------------------------------------------------
 
 @pytest.mark.parametrize("causal", [False, True])
