@@ -5,6 +5,9 @@
 A step is one forward pass (one ``fa_fwd`` launch) over the whole workload
 with Q, K, V already resident in HBM.  W untimed steps, then exactly K timed
 steps bracketed by device synchronisation; rank 0 prints one JSON line.
+Without the flags, W covers at least 0.2 s and K at least 0.1 s of launches
+(and at least 5 and 50 of them): the shader clock settles under a
+continuous load only after some tens of milliseconds.
 
 Throughput counts the two matmuls only: 4*B*H*Lq*Lk*d flops, halved for
 causal ("第 08 章: Flash Attention——分块注意力" (chuoer47.github.io), its
@@ -32,6 +35,7 @@ import ctypes
 import glob
 import hashlib
 import json
+import math
 import os
 import re
 import shutil
@@ -358,6 +362,44 @@ def cpu_baseline_bwd(w, causal, q, k, v, do, grads, budget_s=15.0, max_heads=Non
         "slices": done}
 
 
+# Default launch counts.  Under a continuous load the GPU's clock takes
+# tens of milliseconds to settle: launch durations first rise, then fall to
+# a steady value (bench workload: ≈ 1.2 ms at the fourth launch, steady
+# from about the thirtieth).  The default warm-up therefore runs for a
+# fixed time rather than a fixed count, and the timed launches cover a
+# fixed minimum time as well.
+MIN_WARMUP, WARMUP_S = 5, 0.2
+MIN_STEPS, TIMED_S = 50, 0.1
+
+
+def warm_up(fn, args, n=None):
+    """Untimed launches of fn(*args): exactly n if given, else at least
+    MIN_WARMUP and at least WARMUP_S seconds of them.  Returns (launches,
+    seconds per launch measured after the first one)."""
+    import torch
+    if n == 0:
+        return 0, None
+    fn(*args)                       # first launch: loads code, faults in pages
+    torch.cuda.synchronize()
+    t0, done, target = time.perf_counter(), 1, n
+    batch = 1
+    while True:
+        if target is not None and done >= target:
+            break
+        k = batch if target is None else min(batch, target - done)
+        for _ in range(k):
+            fn(*args)
+        torch.cuda.synchronize()
+        done += k
+        spent = time.perf_counter() - t0
+        per = spent / (done - 1)
+        if target is None and done >= MIN_WARMUP and spent >= WARMUP_S:
+            break
+        batch = max(1, min(4 * batch, math.ceil((WARMUP_S - spent) / per)))
+    per = (time.perf_counter() - t0) / (done - 1) if done > 1 else None
+    return done, per
+
+
 def copy_calibration(mib: int, steps: int, warmup: int) -> int:
     """Plain copy of a known byte count: reads and writes mib MiB per step."""
     import torch
@@ -383,8 +425,12 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed launches (default: at least %d, and at least %.1f s of "
+                         "them)" % (MIN_STEPS, TIMED_S))
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches before them (default: at least %d, and at "
+                         "least %.1f s of them)" % (MIN_WARMUP, WARMUP_S))
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=["causal", "noncausal", "window", "splitkv", "bwd"],
                     default=None,
@@ -412,7 +458,8 @@ def main(argv=None):
 
     import torch
     if a.copy_calibration:
-        return copy_calibration(a.copy_calibration, a.steps, a.warmup)
+        return copy_calibration(a.copy_calibration, a.steps or MIN_STEPS,
+                                MIN_WARMUP if a.warmup is None else a.warmup)
     import exact_io_aware_08_amd as fa
     from seeded_inputs import WORKLOADS, workload_inputs
 
@@ -433,7 +480,7 @@ def main(argv=None):
     fp8 = w.dtype == "fp8"
     if fp8 and mode not in ("causal", "noncausal"):
         raise SystemExit("the FP8 forward has causal and non-causal modes only")
-    log(f"bench: workload {w.name} mode {mode} steps {a.steps} warmup {a.warmup}")
+    log(f"bench: workload {w.name} mode {mode}")
     if fp8:
         q, k, v, descales = workload_inputs(w)
         qd, kd, vd = (torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q, k, v))
@@ -481,9 +528,11 @@ def main(argv=None):
         args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal),
                 w.scale, stream)
 
-    for _ in range(a.warmup):
-        fn(*args)
-    torch.cuda.synchronize()
+    a.warmup, per_launch = warm_up(fn, args, a.warmup)
+    if a.steps is None:
+        a.steps = MIN_STEPS if per_launch is None else max(MIN_STEPS,
+                                                           math.ceil(TIMED_S / per_launch))
+    log(f"bench: warm-up {a.warmup} launches, timing {a.steps}")
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
     torch.cuda.synchronize()

@@ -151,3 +151,29 @@ def test_counters_in_run_sums_the_kernels_of_a_call(monkeypatch):
     assert r2["mfma_busy"] == 0.35 and r2["hbm_bytes_per_launch"] == r["hbm_bytes_per_launch"]
     monkeypatch.setattr(bench.shutil, "which", lambda name: None)
     assert bench.counters_in_run(["--workload", "w"], ["fa_a_kernel"]) is None
+
+
+def test_warm_up_counts(monkeypatch):
+    """The warm-up runs exactly the launches asked for; by default at least
+    MIN_WARMUP of them and at least WARMUP_S seconds' worth."""
+    import time as _time
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    calls = []
+
+    def launch():
+        calls.append(1)
+        _time.sleep(0.002)
+
+    for n in (0, 1, 3, 7):
+        calls.clear()
+        done, per = bench.warm_up(launch, (), n)
+        assert done == n == len(calls)
+        assert (per is None) == (n <= 1)
+    monkeypatch.setattr(bench, "WARMUP_S", 0.05)
+    calls.clear()
+    t0 = _time.perf_counter()
+    done, per = bench.warm_up(launch, ())
+    assert done == len(calls) >= bench.MIN_WARMUP
+    assert _time.perf_counter() - t0 >= 0.05
+    assert 0.0015 < per < 0.02
