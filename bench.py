@@ -475,7 +475,7 @@ def main(argv=None):
 
     w = WORKLOADS[a.workload]
     mode = a.mode or w.modes[0]
-    causal = mode == "causal" or (mode == "bwd" and "causal" in w.modes)
+    causal = mode == "causal" or (mode in ("bwd", "splitkv") and "causal" in w.modes)
     window = w.window if mode == "window" else None
     fp8 = w.dtype == "fp8"
     if fp8 and mode not in ("causal", "noncausal"):
@@ -521,7 +521,7 @@ def main(argv=None):
         nbytes = fa.splitkv_workspace_size(w.B, w.H, w.Lq, w.d, splits)
         ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")   # caller-owned scratch
         fn = fa.fa_fwd_splitkv
-        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, 0, w.scale, splits,
+        args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal), w.scale, splits,
                 ws, nbytes, stream)
     else:
         fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
@@ -559,7 +559,7 @@ def main(argv=None):
     unsplit_ms = None
     if splits:
         # the same inputs through the unsplit kernel, for reference
-        ref_args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, 0, w.scale, stream)
+        ref_args = (qd, kd, vd, od, ld, w.B, w.H, w.Lq, w.Lk, w.d, int(causal), w.scale, stream)
         for _ in range(2):
             fa.fa_fwd(*ref_args)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

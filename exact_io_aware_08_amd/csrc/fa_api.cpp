@@ -334,14 +334,27 @@ int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_
     fa::TileConfig tc;
     if (!fa::tile_config(fa::DType::BF16, d, &tc)) return 0;
     if (num_cus <= 0 && (num_cus = fa::cu_count()) <= 0) return 0;
-    const long long base = (long long)B * H * (((long long)Lq + tc.block_m - 1) / tc.block_m);
-    if (base >= num_cus) return 1;
+    const long long nqb = ((long long)Lq + tc.block_m - 1) / tc.block_m;
+    const long long base = (long long)B * H * nqb;
     // key tiles of the longest query block (causal: it sees min(Lk, Lq) keys)
     const long long keys = causal ? std::min<long long>(Lk, Lq) : Lk;
     const long long tiles = (keys + tc.block_n - 1) / tc.block_n;
-    long long splits = (num_cus + base - 1) / base;
+    long long splits;
+    if (!causal) {
+        // equal blocks: enough workgroups for every compute unit
+        if (base >= num_cus) return 1;
+        splits = (num_cus + base - 1) / base;
+    } else {
+        // causal block i sees min(Lk, (i + 1) block_m) keys; the longest
+        // block's share of tiles should not exceed the mean per compute unit
+        long long total = 0;
+        for (long long i = 0; i < nqb; ++i)
+            total += (std::min<long long>(Lk, (i + 1) * tc.block_m) + tc.block_n - 1) / tc.block_n;
+        total *= (long long)B * H;
+        splits = (tiles * num_cus + total - 1) / total;
+    }
     splits = std::min<long long>(splits, std::max<long long>(1, tiles / 8));
-    return (int)std::min<long long>(splits, kMaxSplits);
+    return (int)std::max<long long>(1, std::min<long long>(splits, kMaxSplits));
 }
 
 int fa_tile_config(int dtype, int d, int* block_m, int* block_n, int* threads) {

@@ -169,13 +169,15 @@ size_t fa_noalloc_scratch_bytes(void);
  * (B, H, Lq < 1, d not 64/128/256, num_splits outside 1 .. 64).  Host-only. */
 size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits);
 
-/* A num_splits for fa_fwd_splitkv on this shape: 1 when the unsplit grid
- * (B * H query blocks) already gives every compute unit a workgroup,
- * else enough splits that the (query block, split) workgroups cover
- * `num_cus` compute units, with at least 8 key tiles per split and at
- * most 64 splits.  num_cus <= 0 reads the current device's count.  Returns
- * 0 for invalid arguments (as fa_fwd's shape checks) or when the device
- * cannot be queried.  Host-only; no GPU work. */
+/* A num_splits for fa_fwd_splitkv on this shape.  Non-causal: 1 when the
+ * unsplit grid (B * H * query blocks) already gives every compute unit a
+ * workgroup, else enough splits that the (query block, split) workgroups
+ * cover `num_cus` compute units.  Causal (blocks of unequal length): enough
+ * splits that the longest block's share of key tiles is at most the mean
+ * number of tiles per compute unit.  Either way at least 8 key tiles per
+ * split and at most 64 splits.  num_cus <= 0 reads the current device's
+ * count.  Returns 0 for invalid arguments (as fa_fwd's shape checks) or
+ * when the device cannot be queried.  Host-only; no GPU work. */
 int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_cus);
 
 /*

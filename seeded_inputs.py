@@ -70,6 +70,11 @@ WORKLOADS = {
     "bf16_longkv_512x64k_d128": Workload("bf16_longkv_512x64k_d128", 1, 16, 512,
                                          65536, 128, "bf16", ("splitkv",), 7,
                                          splits=8),
+    # one GPU's share of the 16K causal workload when its 16 heads are split
+    # over 8 GPUs: 128 query blocks for 256 CUs, so the keys are split (4
+    # splits, the fastest of 1..8 measured, and fa_splitkv_suggest's choice)
+    "bf16_causal_16k_d128_2h": Workload("bf16_causal_16k_d128_2h", 1, 2, 16384, 16384, 128,
+                                        "bf16", ("splitkv", "causal"), 9, splits=4),
     # FP8 E4M3 inputs (per-tensor descale) at the 16K causal shape, the
     # pages' FP8 variant ("Flash Attention 原理与实现详解" (tbr8.org), section
     # 4.3 "FP8 支持")

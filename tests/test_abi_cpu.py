@@ -277,7 +277,10 @@ def test_fp8_validation_errors():
     ((2, 16, 1024, 16384, 128, 0), 2),
     ((1, 4, 64, 131072, 64, 0), 64),       # capped at 64
     ((1, 2, 512, 8000, 256, 0), 31),       # capped at 8 tiles per split (250 tiles of 32)
-    ((1, 4, 4096, 4096, 128, 1), 4),       # causal: the longest block's 32 tiles
+    ((1, 4, 4096, 4096, 128, 1), 4),       # causal: capped at 8 of the longest block's 32 tiles
+    ((1, 2, 16384, 16384, 128, 1), 4),     # causal: 128 longest / (8320 tiles / 256 CUs)
+    ((1, 4, 16384, 16384, 128, 1), 2),     # causal: 256 blocks, the longest twice the mean
+    ((1, 16, 16384, 16384, 128, 1), 1),    # causal: 1024 blocks balance on their own
     ((4, 16, 2048, 8192, 128, 0), 1),      # 512 query blocks already fill 256 CUs
     ((1, 1, 100, 100, 128, 0), 1),         # too few tiles to split
 ])

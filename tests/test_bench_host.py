@@ -19,6 +19,13 @@ def test_flops_match_the_formula():
     assert bench.flops_of(w, False) == 2 * bench.flops_of(w, True)
 
 
+def test_share_workload_is_an_eighth_of_the_bench_one():
+    # one GPU's 2 of the bench workload's 16 heads; causal, split 4 ways
+    w8, w = WORKLOADS["bf16_causal_16k_d128"], WORKLOADS["bf16_causal_16k_d128_2h"]
+    assert bench.flops_of(w, True) * 8 == bench.flops_of(w8, True)
+    assert (w.modes, w.splits) == (("splitkv", "causal"), 4)
+
+
 @pytest.mark.parametrize("name,mb", [("bf16_causal_1k_d64", 33.8), ("bf16_4k_d128", 269.5),
                                      ("bf16_causal_16k_d128", 269.5),
                                      ("bf16_peaky_d256_ragged", 132.9)])

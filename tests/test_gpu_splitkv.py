@@ -123,6 +123,22 @@ def test_longkv_workload_full():
     check_parity(O, LSE, O_ref, L_ref, "bf16", w.name)
 
 
+def test_causal_share_workload_full():
+    """One GPU's share of the 16K causal workload (B=1, H=2, L=16384,
+    d=128), split 4 ways as the bench runs it, every row against the
+    oracle; on a 256-CU device fa_splitkv_suggest picks those 4 splits."""
+    import torch
+    w = WORKLOADS["bf16_causal_16k_d128_2h"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus == 256:
+        assert fa.splitkv_suggest(w.B, w.H, w.Lq, w.Lk, w.d, True) == w.splits
+    q, k, v = workload_inputs(w)
+    say(f"case {w.name} (full size, all rows, {w.splits} causal splits)")
+    O, LSE, _, _ = run_split(q, k, v, True, w.scale, w.splits)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), True, w.scale)
+    check_parity(O, LSE, O_ref, L_ref, "bf16", w.name)
+
+
 def test_suggested_split_on_this_device():
     """fa_splitkv_suggest with the device's own CU count (num_cus = 0), then
     fa_fwd_splitkv with that many splits, against the oracle."""
