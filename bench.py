@@ -157,12 +157,13 @@ def device_peak(cus: int):
     return out
 
 
-# counters of the in-run pass (one rocprofv3 run each; FETCH_SIZE reads half
-# the bytes a copy of known size moves, WRITE_SIZE all of them, so the byte
-# counters are scaled by 2 and 1)
+# counters of the in-run pass (one rocprofv3 run each).  The byte counters
+# are scaled by what they read for a plain copy of known size, measured in
+# the same call (FETCH_SIZE has read half the copied bytes, WRITE_SIZE all
+# of them).
 COUNTER_PASSES = (("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"), ("FETCH_SIZE",),
                   ("WRITE_SIZE",))
-FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+CALIBRATION_MIB = 256
 
 
 def counters_in_run(argv, kernels):
@@ -175,29 +176,54 @@ def counters_in_run(argv, kernels):
     rp = shutil.which("rocprofv3")
     if rp is None:
         return None
+
+    def passes(child, counter_sets):
+        found = []   # (kernel name, counter name, value) of every dispatch
+        for counters in counter_sets:
+            with tempfile.TemporaryDirectory() as d:
+                cmd = [rp, "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "c",
+                       "--", *child]
+                subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
+                               timeout=300, cwd=tempfile.gettempdir())
+                for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"),
+                                   recursive=True):
+                    for r in csv.DictReader(open(f)):
+                        found.append((r["Kernel_Name"], r["Counter_Name"],
+                                      float(r["Counter_Value"])))
+        return found
+
+    me = [sys.executable, os.path.abspath(__file__)]
     vals = {}   # (kernel, counter) -> values
-    child = [sys.executable, os.path.abspath(__file__), *argv, "--steps", "3", "--warmup", "1",
-             "--no-cpu-baseline", "--no-counters"]
-    for counters in COUNTER_PASSES:
-        with tempfile.TemporaryDirectory() as d:
-            cmd = [rp, "--pmc", *counters, "--output-format", "csv", "-d", d, "-o", "c",
-                   "--", *child]
-            subprocess.run(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL,
-                           timeout=300, cwd=tempfile.gettempdir())
-            for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-                for r in csv.DictReader(open(f)):
-                    for kn in kernels:
-                        if all(part in r["Kernel_Name"] for part in kn.split("&")):
-                            vals.setdefault((kn, r["Counter_Name"]), []).append(
-                                float(r["Counter_Value"]))
+    for name, counter, value in passes(me + [*argv, "--steps", "3", "--warmup", "1",
+                                             "--no-cpu-baseline", "--no-counters"],
+                              COUNTER_PASSES):
+        for kn in kernels:
+            if all(part in name for part in kn.split("&")):
+                vals.setdefault((kn, counter), []).append(value)
     need = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "FETCH_SIZE", "WRITE_SIZE")
     if not all(vals.get((kn, n)) for kn in kernels for n in need):
         return None
+    # the copy of known size: CALIBRATION_MIB MiB read and written per
+    # dispatch of the copy kernel (the fill that creates its source is not
+    # counted)
+    cal = {}
+    for name, counter, value in passes(me + ["--copy-calibration", str(CALIBRATION_MIB),
+                                             "--steps", "3", "--warmup", "1"],
+                                       (("FETCH_SIZE",), ("WRITE_SIZE",))):
+        if "copy" in name.lower():
+            cal.setdefault(counter, []).append(value)
+    if not (cal.get("FETCH_SIZE") and cal.get("WRITE_SIZE")):
+        return None
+    known_kib = CALIBRATION_MIB * 1024.0
+    fetch_scale = known_kib / float(np.mean(cal["FETCH_SIZE"]))
+    write_scale = known_kib / float(np.mean(cal["WRITE_SIZE"]))
     tot = {n: sum(float(np.mean(vals[(kn, n)])) for kn in kernels) for n in need}
     cycles = tot["GRBM_GUI_ACTIVE"] / 8          # summed over the 8 XCDs
     return {"mfma_busy": round(tot["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * cycles), 4),
-            "hbm_bytes_per_launch": (FETCH_SCALE * tot["FETCH_SIZE"] +
-                                     WRITE_SCALE * tot["WRITE_SIZE"]) * 1024,
+            "hbm_bytes_per_launch": (fetch_scale * tot["FETCH_SIZE"] +
+                                     write_scale * tot["WRITE_SIZE"]) * 1024,
+            "copy_calibration": {"mib": CALIBRATION_MIB, "fetch_scale": round(fetch_scale, 4),
+                                 "write_scale": round(write_scale, 4)},
             "kernels": list(kernels),
             "passes": [" ".join(c) for c in COUNTER_PASSES]}
 

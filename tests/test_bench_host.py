@@ -119,9 +119,13 @@ def test_counters_in_run_sums_the_kernels_of_a_call(monkeypatch):
     """The in-run counter passes average each counter over each named
     kernel's dispatches and sum the averages over the kernels of one call;
     MFMA busy is busy cycles over 1024 SIMDs x kernel cycles (GRBM_GUI_ACTIVE
-    summed over the 8 XCDs), HBM bytes are FETCH_SIZE x 2 + WRITE_SIZE x 1
-    KiB.  rocprofv3 is replaced by a writer of its CSV."""
+    summed over the 8 XCDs), HBM bytes are FETCH_SIZE and WRITE_SIZE KiB
+    scaled by what they read for the copy of known size in the same call
+    (here half and all of its bytes: factors 2 and 1).  rocprofv3 is
+    replaced by a writer of its CSV."""
     import csv as _csv
+    known = bench.CALIBRATION_MIB * 1024.0
+    copy_reads = {"FETCH_SIZE": [known / 2, known / 2], "WRITE_SIZE": [known, known]}
     values = {  # per kernel: counter -> per-dispatch values
         "fa_a_kernel<1>": {"SQ_VALU_MFMA_BUSY_CYCLES": [1024 * 800.0, 1024 * 600.0],
                            "GRBM_GUI_ACTIVE": [8 * 1000.0, 8 * 1000.0],
@@ -139,6 +143,13 @@ def test_counters_in_run_sums_the_kernels_of_a_call(monkeypatch):
         with open(os.path.join(d, "c_counter_collection.csv"), "w", newline="") as f:
             wr = _csv.writer(f)
             wr.writerow(["Kernel_Name", "Counter_Name", "Counter_Value"])
+            if "--copy-calibration" in cmd:
+                for c in pmc:
+                    # the fill that creates the copy's source is not counted
+                    wr.writerow(["vectorized_elementwise_kernel<FillFunctor>", c, 3.0])
+                    for x in copy_reads[c]:
+                        wr.writerow(["__amd_rocclr_copyBuffer", c, x])
+                return
             for kn, cv in values.items():
                 for c in pmc:
                     for x in cv[c]:
@@ -156,6 +167,11 @@ def test_counters_in_run_sums_the_kernels_of_a_call(monkeypatch):
     values["fa_a_kernel<2>"] = {k: [x * 9 for x in v] for k, v in values["fa_a_kernel<1>"].items()}
     r2 = bench.counters_in_run(["--workload", "w"], ["fa_a_kernel&<1>", "fa_b_kernel"])
     assert r2["mfma_busy"] == 0.35 and r2["hbm_bytes_per_launch"] == r["hbm_bytes_per_launch"]
+    # a counter that reads 2/5 of the copied bytes is scaled by 2.5
+    copy_reads["FETCH_SIZE"] = [known * 0.4]
+    r3 = bench.counters_in_run(["--workload", "w"], ["fa_a_kernel&<1>", "fa_b_kernel"])
+    assert r3["hbm_bytes_per_launch"] == pytest.approx((210 * 2.5 + 55) * 1024)
+    assert r3["copy_calibration"]["fetch_scale"] == 2.5
     monkeypatch.setattr(bench.shutil, "which", lambda name: None)
     assert bench.counters_in_run(["--workload", "w"], ["fa_a_kernel"]) is None
 
@@ -184,3 +200,4 @@ def test_warm_up_counts(monkeypatch):
     assert done == len(calls) >= bench.MIN_WARMUP
     assert _time.perf_counter() - t0 >= 0.05
     assert 0.0015 < per < 0.02
+
