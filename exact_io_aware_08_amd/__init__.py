@@ -267,7 +267,9 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
     right) sliding window, None on a side for no bound (bf16 only; combined
     with ``causal`` the right bound is 0).  ``num_splits``: split the keys
     among that many workgroups per query block and merge (bf16 only; the
-    workspace is allocated with torch).  Returns (O, LSE)."""
+    workspace is allocated with torch); ``"auto"``: the count
+    ``splitkv_suggest`` gives for this shape on this device, no split when it
+    gives 1 (or for fp32 inputs or a window).  Returns (O, LSE)."""
     import torch
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B, H, L, d]")
@@ -279,6 +281,14 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None,
         raise ValueError("k and v must be [B, H, Lk, d] matching q")
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    if isinstance(num_splits, str):
+        if num_splits != "auto":
+            raise ValueError(f"num_splits must be an int, None or 'auto', not {num_splits!r}")
+        num_splits = None
+        if q.dtype == torch.bfloat16 and window is None:
+            n = splitkv_suggest(B, H, Lq, Lk, d, causal)
+            if n > 1:
+                num_splits = n
     current = torch.cuda.current_stream(q.device)
     if stream is None:
         stream = current

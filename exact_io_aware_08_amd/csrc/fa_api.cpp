@@ -354,6 +354,9 @@ int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_
         splits = (tiles * num_cus + total - 1) / total;
     }
     splits = std::min<long long>(splits, std::max<long long>(1, tiles / 8));
+    // at d = 64 the unsplit kernel already runs two key halves per block on
+    // grids of at most two workgroups per compute unit (merged on chip)
+    if (d == 64 && base <= 2LL * num_cus && splits <= 2) return 1;
     return (int)std::max<long long>(1, std::min<long long>(splits, kMaxSplits));
 }
 

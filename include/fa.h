@@ -175,7 +175,9 @@ size_t fa_splitkv_workspace_size(int B, int H, int Lq, int d, int num_splits);
  * cover `num_cus` compute units.  Causal (blocks of unequal length): enough
  * splits that the longest block's share of key tiles is at most the mean
  * number of tiles per compute unit.  Either way at least 8 key tiles per
- * split and at most 64 splits.  num_cus <= 0 reads the current device's
+ * split and at most 64 splits; 1 instead of 2 at d = 64 when the unsplit
+ * kernel already splits each block's keys in two (grids of at most two
+ * workgroups per compute unit).  num_cus <= 0 reads the current device's
  * count.  Returns 0 for invalid arguments (as fa_fwd's shape checks) or
  * when the device cannot be queried.  Host-only; no GPU work. */
 int fa_splitkv_suggest(int B, int H, int Lq, int Lk, int d, int causal, int num_cus);

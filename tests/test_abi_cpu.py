@@ -283,6 +283,12 @@ def test_fp8_validation_errors():
     ((1, 16, 16384, 16384, 128, 1), 1),    # causal: 1024 blocks balance on their own
     ((4, 16, 2048, 8192, 128, 0), 1),      # 512 query blocks already fill 256 CUs
     ((1, 1, 100, 100, 128, 0), 1),         # too few tiles to split
+    ((4, 16, 1024, 1024, 64, 1), 1),       # causal d = 64: 512 blocks, 16 tiles at most
+    ((2, 16, 1024, 1024, 64, 1), 1),       # 2 by the causal rule; key halves already
+    ((1, 4, 4096, 4096, 64, 1), 4),        # 64 longest / (4224 tiles / 256 CUs)
+    ((1, 8, 128, 8192, 64, 0), 16),        # 32 by the CU rule, capped at 8 of 128 tiles
+    ((1, 16, 1024, 2048, 64, 0), 1),       # 128 blocks: 2 by the CU rule; key halves already
+    ((1, 16, 1024, 2048, 128, 0), 2),      # d = 128: 64 blocks, 4 by the CU rule, capped at 16 / 8
 ])
 def test_splitkv_suggest(shape, want):
     assert fa.splitkv_suggest(*shape, num_cus=256) == want
@@ -292,3 +298,12 @@ def test_splitkv_suggest_invalid():
     assert fa.splitkv_suggest(0, 1, 8, 8, 128, 0, 256) == 0
     assert fa.splitkv_suggest(1, 1, 8, 8, 96, 0, 256) == 0
     assert fa.splitkv_suggest(1, 1, 8, 8, 128, 2, 256) == 0
+
+
+def test_attention_rejects_unknown_split_mode():
+    """num_splits takes an int, None or 'auto'; any other string is refused
+    before any GPU work."""
+    import torch
+    x = torch.zeros((1, 1, 4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="num_splits"):
+        fa.attention(x, x, x, num_splits="fastest")

@@ -282,3 +282,29 @@ def test_attention_wrapper_matches_abi():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(o2.view(torch.int16).cpu().numpy().view(np.uint16), O)
     np.testing.assert_array_equal(l2.cpu().numpy(), L)
+
+
+def test_attention_auto_splits_follow_the_suggestion():
+    """num_splits='auto': the key split at fa_splitkv_suggest's count where
+    it is above 1 (bit for bit the explicit call), the unsplit kernel
+    where it is 1."""
+    import torch
+    q, k, v = make_inputs(38, 1, 4, 256, 4096, 128, "bf16")
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    n = fa.splitkv_suggest(1, 4, 256, 4096, 128, False)
+    assert n > 1
+    o_a, l_a = fa.attention(qd, kd, vd, causal=False, num_splits="auto")
+    o_n, l_n = fa.attention(qd, kd, vd, causal=False, num_splits=n)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_n) and torch.equal(l_a, l_n)
+    O_ref, L_ref = attention_ref(widen(q), widen(k), widen(v), False, f32_scale(128))
+    O = widen(o_a.view(torch.int16).cpu().numpy().view(np.uint16))
+    assert np.abs(O - O_ref).max() <= 2e-2
+    assert np.abs(l_a.cpu().numpy() - L_ref).max() <= 1e-3
+    q, k, v = make_inputs(39, 2, 16, 1024, 1024, 64, "bf16")
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    assert fa.splitkv_suggest(2, 16, 1024, 1024, 64, True) == 1
+    o_a, l_a = fa.attention(qd, kd, vd, causal=True, num_splits="auto")
+    o_u, l_u = fa.attention(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_u) and torch.equal(l_a, l_u)
